@@ -1,0 +1,175 @@
+"""Benchmark of causal GQA prefill attention on one MI355X.
+
+A step is one gqa_attn_prefill call (the whole hot path: Q load/quantise, K/V
+tile fetch, Q·K^T, scale and causal mask, online softmax, P·V, epilogue) over
+the q_len 4096 x kv_len 32768 chunk (24 query heads, 4 KV heads, head_dim 256,
+bf16, contiguous KV) unless --workload says otherwise. Inputs are seeded
+synthetic tensors already resident in HBM when the timed region starts.
+
+Prints one JSON line: TFLOP/s counted causal-effectively (4 * 24 * 256 * the
+number of visible query/key pairs per head, divided by the time), the roofline
+of the kernel against the MI355X dense bf16 MFMA peak, and the CPU oracle timed
+on a bounded sample of the same workload as a baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GQA causal prefill attn TFLOP/s + % MFMA peak, q4096×kv32K, 24Q/4KV d256"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk (the published 2.5 PFLOP/s dense)
+PEAK_INT8_TOPS = 5033.2
+HQ, HKV, D = 24, 4, 256
+KERNEL_SOURCE = os.path.join(ROOT, "gqa_causal_prefill_amd", "csrc", "gqa_prefill.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3,
+                    help="1 tiny, 2 4096x8192, 3 4096x32768 (default), 4 paged 512x32768, "
+                         "5 int8-k 3072x16384, 6 4096x16384")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="query rows of the workload the CPU oracle computes (all 24 heads)")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload_name: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, d, rows_n):
+    """Oracle time on the last `rows_n` query rows (x 24 heads) of the workload."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    rows = np.arange(w.q_len - rows_n, w.q_len)
+    off = w.kv_len - w.q_len
+    pairs = int(np.sum(off + rows + 1))
+    flops = 4.0 * HQ * D * pairs
+    t = time.perf_counter()
+    if w.int8k:
+        kq, ks = oracle.quantize_rows_int8(d["k"])
+        oracle.attention_int8k(d["q"], kq, ks, d["v"], rows=rows)
+    else:
+        oracle.attention(d["q"], d["k"], d["v"], rows=rows)
+    dt = time.perf_counter() - t
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"query rows {rows[0]}..{rows[-1]} ({rows_n} rows) x 24 heads of {w.name}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
+                                   f"--gpus {args.gpus} is not supported"}))
+        sys.exit(2)
+    import torch
+
+    import gqa_causal_prefill_amd as gqa
+    from gqa_synth import WORKLOADS, make_workload
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    print(f"bench: {w.name} generating inputs", file=sys.stderr, flush=True)
+    d = make_workload(w)
+    q = d["q"].to(dev)
+    v = (d["v_cache"] if w.paged else d["v"]).to(dev)
+    kw = {}
+    if w.paged:
+        k = d["k_cache"].to(dev)
+        kw = dict(block_table=d["block_table"].to(dev), kv_len=w.kv_len)
+    elif w.int8k:
+        k, ks = gqa.gqa_quantize_rows_int8(d["k"].to(dev))
+        kw = dict(k_scale=ks)
+    else:
+        k = d["k"].to(dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gqa.gqa_attn_prefill(q, k, v, out=out, stream=stream, **kw)
+
+    print(f"bench: {w.name} warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    print(f"bench: {w.name} {args.steps} steps, {ms:.4f} ms/step", file=sys.stderr, flush=True)
+
+    flops = 4.0 * HQ * D * w.pairs_per_head
+    tflops = flops / (ms * 1e-3) / 1e12
+    if w.int8k:
+        # Q·K^T on int8 MFMA, P·V on bf16 MFMA: time at peak is the sum of both halves
+        t_peak = (flops / 2) / (PEAK_INT8_TOPS * 1e12) + (flops / 2) / (PEAK_BF16_TFLOPS * 1e12)
+        peak = flops / t_peak / 1e12
+    else:
+        peak = PEAK_BF16_TFLOPS
+    roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": round(peak, 1),
+                "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                "traffic": load_traffic(w.name)}
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+bf16" if w.int8k else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "q_len": w.q_len, "kv_len": w.kv_len, "q_heads": HQ,
+                   "kv_heads": HKV, "head_dim": D,
+                   "kv_layout": "paged16" if w.paged else "contiguous",
+                   "keys": "int8" if w.int8k else "bf16",
+                   "variant": gqa.gqa_attn_prefill_plan(w.q_len, w.kv_len, w.paged, w.int8k)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print(f"bench: cpu oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, d, min(args.cpu_rows, w.q_len))
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

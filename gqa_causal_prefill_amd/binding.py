@@ -1,0 +1,175 @@
+"""ctypes binding of libgqa_prefill.so (argument marshalling only).
+
+Every function has the name of the C entry point it calls. Tensors are torch
+tensors on the GPU; torch supplies device memory and the current stream, the
+HIP library does all the work. There is no fallback: if the library is missing
+or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+from .build import LIB
+
+NUM_Q_HEADS = 24
+NUM_KV_HEADS = 4
+HEAD_DIM = 256
+BLOCK_SIZE = 16
+
+GQA_OK = 0
+_STATUS_NAMES = {
+    0: "GQA_OK",
+    1: "GQA_ERR_NULL_ARG",
+    2: "GQA_ERR_BAD_LENGTH",
+    3: "GQA_ERR_MISALIGNED",
+    4: "GQA_ERR_UNSUPPORTED",
+    5: "GQA_ERR_HIP",
+}
+
+
+class GqaError(RuntimeError):
+    """A non-OK status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS_NAMES.get(status, status)} "
+                         f"({gqa_status_string(status)})")
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libgqa_prefill.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            raise RuntimeError(f"{LIB} is missing: build it with "
+                               "`python -m gqa_causal_prefill_amd.build`")
+        lib = ctypes.CDLL(LIB)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        lib.gqa_abi_version.restype = ctypes.c_int
+        lib.gqa_abi_version.argtypes = []
+        lib.gqa_status_string.restype = ctypes.c_char_p
+        lib.gqa_status_string.argtypes = [ctypes.c_int]
+        lib.gqa_attn_prefill.restype = ctypes.c_int
+        lib.gqa_attn_prefill.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, vp]
+        lib.gqa_quantize_rows_int8.restype = ctypes.c_int
+        lib.gqa_quantize_rows_int8.argtypes = [vp, i64, vp, vp, vp]
+        lib.gqa_attn_prefill_plan.restype = ctypes.c_int
+        lib.gqa_attn_prefill_plan.argtypes = [i32, i32, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_char_p, ctypes.c_size_t]
+        _lib = lib
+    return _lib
+
+
+def gqa_abi_version() -> int:
+    return library().gqa_abi_version()
+
+
+def gqa_status_string(status: int) -> str:
+    return library().gqa_status_string(status).decode()
+
+
+def gqa_attn_prefill_plan(q_len: int, kv_len: int, paged: bool = False, int8k: bool = False) -> str:
+    buf = ctypes.create_string_buffer(256)
+    st = library().gqa_attn_prefill_plan(q_len, kv_len, int(paged), int(int8k), buf, 256)
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_attn_prefill_plan")
+    return buf.value.decode()
+
+
+def _stream_handle(t: torch.Tensor, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _expect(t, name, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def gqa_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     block_table: torch.Tensor | None = None, num_blocks: int | None = None,
+                     k_scale: torch.Tensor | None = None, q_len: int | None = None,
+                     kv_len: int | None = None, out: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """Causal GQA prefill attention; see gqa_attn_prefill in include/gqa_prefill.h.
+
+    q: bf16 [q_len, 24, 256]. Contiguous: k, v [kv_len, 4, 256]. Paged (block_table
+    given): k, v caches [num_blocks, 4, 16, 256] and block_table int32
+    [ceil(kv_len / 16)] (kv_len must then be given). INT8 keys: k int8 and
+    k_scale float32 [kv_len, 4]. Returns out (bf16 [q_len, 24, 256]).
+    """
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gqa_attn_prefill runs on the GPU; q is on " + str(dev))
+    q_len = q.shape[0] if q_len is None else q_len
+    paged = block_table is not None
+    if paged:
+        if kv_len is None:
+            raise ValueError("kv_len is required with a block table")
+        nb = k.shape[0] if num_blocks is None else num_blocks
+        _expect(block_table, "block_table", torch.int32, (math.ceil(kv_len / BLOCK_SIZE),), dev)
+        cache_shape = (nb, NUM_KV_HEADS, BLOCK_SIZE, HEAD_DIM)
+        k_shape = v_shape = cache_shape
+    else:
+        kv_len = k.shape[0] if kv_len is None else kv_len
+        nb = 0
+        k_shape = v_shape = (kv_len, NUM_KV_HEADS, HEAD_DIM)
+    _expect(q, "q", torch.bfloat16, (q_len, NUM_Q_HEADS, HEAD_DIM), dev)
+    _expect(k, "k", torch.int8 if k_scale is not None else torch.bfloat16, k_shape, dev)
+    _expect(v, "v", torch.bfloat16, v_shape, dev)
+    if k_scale is not None:
+        _expect(k_scale, "k_scale", torch.float32, (kv_len, NUM_KV_HEADS), dev)
+    if out is None:
+        out = torch.empty((q_len, NUM_Q_HEADS, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    else:
+        _expect(out, "out", torch.bfloat16, (q_len, NUM_Q_HEADS, HEAD_DIM), dev)
+    st = library().gqa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(block_table), nb,
+                                    _ptr(k_scale), q_len, kv_len, _ptr(out),
+                                    _stream_handle(q, stream))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_attn_prefill")
+    return out
+
+
+def gqa_quantize_rows_int8(x: torch.Tensor, xq: torch.Tensor | None = None,
+                           scale: torch.Tensor | None = None, stream=None):
+    """Per-row INT8 quantisation of bf16 rows of 256; returns (xq int8, scale float32).
+
+    x may have any leading shape [..., 256]; xq has x's shape and scale its
+    leading shape.
+    """
+    if x.device.type != "cuda":
+        raise ValueError("gqa_quantize_rows_int8 runs on the GPU")
+    if x.dtype != torch.bfloat16 or x.shape[-1] != HEAD_DIM or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 tensor [..., 256]")
+    rows = x.numel() // HEAD_DIM
+    if xq is None:
+        xq = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _expect(xq, "xq", torch.int8, x.shape, x.device)
+    _expect(scale, "scale", torch.float32, x.shape[:-1], x.device)
+    st = library().gqa_quantize_rows_int8(_ptr(x), rows, _ptr(xq), _ptr(scale),
+                                          _stream_handle(x, stream))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_quantize_rows_int8")
+    return xq, scale

@@ -1,0 +1,61 @@
+"""Compile the HIP sources of this package for gfx950 with hipcc.
+
+Produces, next to this file:
+  libgqa_prefill.so       the C-ABI library declared in include/gqa_prefill.h
+  libgqa_layout_probe.so  a test-only library with one MFMA per entry point, used
+                          to check the CPU model of the gfx950 MFMA register layouts
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+
+LIB = os.path.join(PKG, "libgqa_prefill.so")
+PROBE_LIB = os.path.join(PKG, "libgqa_layout_probe.so")
+
+# -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in any generated code.
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def _compile(sources, output, verbose=False):
+    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", "-o", output + ".tmp", *sources]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines()
+            if "not a recognized feature" not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(output + ".tmp", output)
+
+
+def build(verbose: bool = False) -> None:
+    """Compile both libraries (always, even if they exist)."""
+    _compile([os.path.join(CSRC, "gqa_prefill.hip")], LIB, verbose)
+    _compile([os.path.join(CSRC, "layout_probe.hip")], PROBE_LIB, verbose)
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    print("built", LIB, "and", PROBE_LIB)

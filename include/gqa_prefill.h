@@ -1,0 +1,141 @@
+/*
+ * gqa_prefill.h - causal grouped-query prefill attention for MI355X (gfx950).
+ *
+ * The operation (as the pages state it; cited by page title and section):
+ *   - "DCU使用技术报告（中篇）" §1-§2: one sequence, BF16, 24 query heads over 4 KV
+ *     heads (GQA ratio 6), head_dim 256; the prefill kernel computes Q·Kᵀ, the
+ *     causal mask, an online softmax and P·V with FP32 accumulation; shapes it
+ *     does not support are refused, never run with a wrong mapping (§2, and
+ *     "gfx936 DCU上实现INT8 QK MMAC" §7).
+ *   - "gfx936 DCU上实现INT8 QK MMAC" §1: score = Q·Kᵀ/sqrt(256); with INT8 keys,
+ *     Q ≈ Qq·sQ, K ≈ Kq·sK and score = int32(Qq·Kqᵀ)·sQ·sK/16, restored per score
+ *     before the softmax; §3: paged K reached through a block table
+ *     (logical token -> physical block -> slot); §4: sQ = max|q|/127,
+ *     Qq = round(q/sQ), computed once per query row; §5.2: query head h reads
+ *     KV head h/6.
+ *   - Chunked prefill with history: the q_len queries are the last q_len
+ *     positions of a kv_len-token sequence; query i sits at position
+ *     kv_len - q_len + i and attends keys 0 .. kv_len - q_len + i.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *     keeps no reference after the call returns and allocates nothing.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously; the library never synchronises.
+ *   - Argument errors are detected on the host before anything is enqueued
+ *     and returned as a gqa_status; nothing is written in that case.
+ *     GQA_ERR_HIP reports a failed launch. A device fault surfaces at the
+ *     caller's next synchronisation, as usual for HIP.
+ *   - Calls hold no global mutable state and are thread-safe.
+ *   - Fixed shape: GQA_NUM_Q_HEADS, GQA_NUM_KV_HEADS, GQA_HEAD_DIM,
+ *     GQA_BLOCK_SIZE below. Layouts are row-major and contiguous.
+ */
+#ifndef GQA_PREFILL_H
+#define GQA_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQA_ABI_VERSION 1
+#define GQA_NUM_Q_HEADS 24
+#define GQA_NUM_KV_HEADS 4
+#define GQA_HEAD_DIM 256
+#define GQA_BLOCK_SIZE 16
+/* largest accepted q_len / kv_len (keeps every device offset inside int64 and
+   every grid inside HIP's limits) */
+#define GQA_MAX_LEN (1 << 24)
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_NULL_ARG = 1,     /* a required pointer is NULL */
+  GQA_ERR_BAD_LENGTH = 2,   /* q_len < 0, kv_len < q_len, a length above GQA_MAX_LEN,
+                               rows < 0, or num_blocks too small for kv_len */
+  GQA_ERR_MISALIGNED = 3,   /* a tensor pointer is not aligned as documented */
+  GQA_ERR_UNSUPPORTED = 4,  /* a combination this library refuses (paged + INT8 K) */
+  GQA_ERR_HIP = 5           /* the HIP launch failed */
+} gqa_status;
+
+/* Version of this interface; equals GQA_ABI_VERSION of the header the library
+   was built with. */
+int gqa_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* gqa_status_string(int status);
+
+/*
+ * gqa_attn_prefill - causal GQA attention for one prefill chunk.
+ *
+ *   out[i, h, :] = sum_j softmax_j(score(i, h, j)) * V[j, h/6, :]
+ *   over keys j = 0 .. kv_len - q_len + i, with score as described above.
+ *
+ * q      bf16 [q_len, 24, 256]; 16-byte aligned.
+ * k, v   block_table == NULL: contiguous [kv_len, 4, 256];
+ *        block_table != NULL: paged caches [num_blocks, 4, 16, 256], logical
+ *        key t at cache[block_table[t / 16], :, t % 16, :].
+ *        v is always bf16. k is bf16 when k_scale == NULL, and int8 codes when
+ *        k_scale != NULL. 16-byte aligned.
+ * block_table  int32 [ceil(kv_len / 16)] or NULL; 4-byte aligned. Entries
+ *        must lie in [0, num_blocks); an entry outside that range is clamped
+ *        into it (the output is then wrong but no memory outside the caches is
+ *        read).
+ * num_blocks   physical blocks in each paged cache; ignored when block_table
+ *        is NULL; must be >= ceil(kv_len / 16) when it is not.
+ * k_scale  float32 [kv_len, 4] (one scale per key token and KV head) or NULL;
+ *        4-byte aligned. With INT8 keys each query row (token, head) is
+ *        quantised inside the call: sQ = max|q| / 127 in float32,
+ *        Qq = round-half-even(q / sQ) (IEEE division), a zero row gives 0.
+ * q_len, kv_len  0 <= q_len <= kv_len <= GQA_MAX_LEN. q_len == 0 is a no-op.
+ * out    bf16 [q_len, 24, 256]; fully overwritten (round-to-nearest-even);
+ *        16-byte aligned; must not overlap q, k, v or the caches.
+ * stream hipStream_t or NULL.
+ *
+ * Returns GQA_OK, GQA_ERR_NULL_ARG, GQA_ERR_BAD_LENGTH, GQA_ERR_MISALIGNED,
+ * GQA_ERR_UNSUPPORTED (paged caches together with INT8 keys) or GQA_ERR_HIP.
+ */
+int gqa_attn_prefill(const void* q, const void* k, const void* v,
+                     const int32_t* block_table, int32_t num_blocks,
+                     const float* k_scale, int32_t q_len, int32_t kv_len,
+                     void* out, void* stream);
+
+/*
+ * gqa_quantize_rows_int8 - the per-row INT8 quantiser of "gfx936 DCU上实现INT8 QK
+ * MMAC" §1/§4 as a standalone step (the K-cache producer's quantisation; the
+ * attention call applies the same rule to Q internally).
+ *
+ * x      bf16 [rows, 256]; 16-byte aligned.
+ * xq     int8 [rows, 256] output; 4-byte aligned.
+ * scale  float32 [rows] output: s = max|x| / 127 (float32 IEEE division);
+ *        xq = clamp(round-half-even(x / s), -127, 127); a zero row gives s = 0
+ *        and xq = 0. 4-byte aligned.
+ * rows   >= 0; rows == 0 is a no-op.
+ *
+ * Returns GQA_OK, GQA_ERR_NULL_ARG, GQA_ERR_BAD_LENGTH, GQA_ERR_MISALIGNED or
+ * GQA_ERR_HIP.
+ */
+int gqa_quantize_rows_int8(const void* x, int64_t rows, void* xq, float* scale,
+                           void* stream);
+
+/*
+ * gqa_attn_prefill_plan - the launch the dispatcher would choose for a call
+ * with these lengths (variant name, workgroup count, threads per workgroup,
+ * bytes of LDS), written as text into buf (at most n bytes, NUL-terminated).
+ * Pure host function: touches no device. The variant depends on the lengths
+ * the same way the pages' dispatch depends on the real q_len and kv_len of a
+ * chunk ("DCU使用技术报告（中篇）" §3, §5).
+ *
+ * paged, int8k: 0 or 1. Returns the same status codes as gqa_attn_prefill
+ * would for these lengths (argument checks only) and GQA_ERR_NULL_ARG when
+ * buf is NULL or n is 0.
+ */
+int gqa_attn_prefill_plan(int32_t q_len, int32_t kv_len, int paged, int int8k,
+                          char* buf, size_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_PREFILL_H */

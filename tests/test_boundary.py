@@ -1,0 +1,133 @@
+"""The C-ABI library on the host: it loads, exports what the header declares and
+rejects bad arguments before touching the GPU (no compute call runs here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gqa_causal_prefill_amd import build as gqa_build
+from gqa_causal_prefill_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER_DIR = os.path.join(ROOT, "include")
+
+OK, NULL, BADLEN, MISALIGNED, UNSUPPORTED, HIPERR = range(6)
+
+
+def _have_lib():
+    return os.path.exists(gqa_build.LIB)
+
+
+pytestmark = pytest.mark.skipif(not _have_lib(), reason="libgqa_prefill.so not built")
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(HEADER_DIR)):
+        if fn.endswith(".h"):
+            text = open(os.path.join(HEADER_DIR, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gqa_\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"gqa_attn_prefill", "gqa_quantize_rows_int8", "gqa_attn_prefill_plan",
+            "gqa_abi_version", "gqa_status_string"} <= set(names)
+    lib = ctypes.CDLL(gqa_build.LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_probe_library_loads():
+    if not os.path.exists(gqa_build.PROBE_LIB):
+        pytest.skip("probe library not built")
+    lib = ctypes.CDLL(gqa_build.PROBE_LIB)
+    assert hasattr(lib, "gqa_probe_mfma_f32_16x16x32_bf16")
+    assert hasattr(lib, "gqa_probe_mfma_i32_16x16x64_i8")
+
+
+def test_abi_version_and_status_strings():
+    assert binding.gqa_abi_version() == 1
+    for s in range(6):
+        assert binding.gqa_status_string(s)
+    assert binding.gqa_status_string(99) == "unknown status"
+
+
+def call(q=16, k=16, v=16, bt=None, nb=0, ks=None, q_len=4, kv_len=8, out=16):
+    lib = binding.library()
+    vp = ctypes.c_void_p
+    return lib.gqa_attn_prefill(vp(q), vp(k), vp(v), vp(bt), nb, vp(ks), q_len, kv_len, vp(out),
+                                None)
+
+
+def test_zero_queries_is_a_noop():
+    # q_len == 0 returns OK without reading any pointer (even NULL ones)
+    assert call(q=None, k=None, v=None, out=None, q_len=0, kv_len=0) == OK
+    assert call(q=None, k=None, v=None, out=None, q_len=0, kv_len=100) == OK
+
+
+@pytest.mark.parametrize("q_len,kv_len", [(-1, 4), (5, 4), (1, -3), (1, (1 << 24) + 1)])
+def test_bad_lengths(q_len, kv_len):
+    assert call(q_len=q_len, kv_len=kv_len) == BADLEN
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "out"])
+def test_null_pointers(which):
+    assert call(**{which: None}) == NULL
+
+
+def test_paged_with_int8_keys_is_refused():
+    assert call(bt=16, nb=1, ks=16) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "out"])
+def test_misaligned_tensors(which):
+    assert call(**{which: 16 + 8}) == MISALIGNED
+
+
+def test_misaligned_small_args():
+    assert call(bt=16 + 2, nb=1) == MISALIGNED
+    assert call(ks=16 + 1) == MISALIGNED
+
+
+def test_too_few_blocks():
+    # kv_len 40 needs ceil(40/16) = 3 blocks
+    assert call(bt=16, nb=2, kv_len=40) == BADLEN
+    assert call(bt=16, nb=0, kv_len=40) == BADLEN
+
+
+def test_quantizer_argument_checks():
+    lib = binding.library()
+    vp = ctypes.c_void_p
+    assert lib.gqa_quantize_rows_int8(None, 0, None, None, None) == OK
+    assert lib.gqa_quantize_rows_int8(vp(16), -1, vp(16), vp(16), None) == BADLEN
+    assert lib.gqa_quantize_rows_int8(None, 4, vp(16), vp(16), None) == NULL
+    assert lib.gqa_quantize_rows_int8(vp(16 + 4), 4, vp(16), vp(16), None) == MISALIGNED
+    assert lib.gqa_quantize_rows_int8(vp(16), 4, vp(16 + 1), vp(16), None) == MISALIGNED
+
+
+def test_plan_describes_the_dispatch():
+    plan = binding.gqa_attn_prefill_plan(4096, 32768)
+    assert "variant=bf16_contiguous" in plan
+    # one workgroup per (KV head, head pair, 64-token block): 4 * 3 * 64
+    assert "workgroups=768" in plan and "threads=256" in plan
+    assert "variant=bf16_paged" in binding.gqa_attn_prefill_plan(512, 32768, paged=True)
+    assert "variant=int8k" in binding.gqa_attn_prefill_plan(3072, 16384, int8k=True)
+    assert "workgroups=12" in binding.gqa_attn_prefill_plan(1, 1)
+    with pytest.raises(binding.GqaError):
+        binding.gqa_attn_prefill_plan(512, 32768, paged=True, int8k=True)
+    with pytest.raises(binding.GqaError):
+        binding.gqa_attn_prefill_plan(10, 5)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(4, 24, 256, dtype=torch.bfloat16)
+    k = torch.zeros(8, 4, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.gqa_attn_prefill(q, k, k)

@@ -1,0 +1,240 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Tolerances (the target stated for this operation): bf16 paths max |err| <= 1e-2
+and mean |err| <= 1e-3 against the float64 oracle; the INT8-K path max |err| <=
+2e-3 against the oracle that applies the same quantisation. Small shapes are
+compared element by element in full; the full-size workloads (in the launch
+configuration the benchmark times) on sampled query rows, all heads, all
+features, which the oracle computes row by row.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_causal_prefill_amd as gqa
+import oracle
+from gqa_synth import WORKLOADS, Workload, make_workload, make_qkv, scatter_paged, block_table_for
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+BF16_MAX, BF16_MEAN, INT8_MAX = 1e-2, 1e-3, 2e-3
+
+
+def note(msg):
+    print(msg, flush=True)
+
+
+def errors(out, ref):
+    e = np.abs(out.detach().cpu().to(torch.float64).numpy() - ref)
+    return float(e.max()), float(e.mean())
+
+
+def sample_rows(q_len, n_random=8, seed=0):
+    rng = np.random.default_rng(seed)
+    fixed = {0, 1, 31, 32, 63, 64, q_len // 2, q_len - 65, q_len - 64, q_len - 2, q_len - 1}
+    rows = sorted({r for r in fixed if 0 <= r < q_len} | set(rng.integers(0, q_len, n_random)))
+    return np.array(rows)
+
+
+def run_contiguous(d):
+    return gqa.gqa_attn_prefill(d["q"].to(DEV), d["k"].to(DEV), d["v"].to(DEV))
+
+
+# ------------------------------------------------------------------ small shapes, full compare
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_tiny_128x128_full(seed):
+    w = Workload("tiny", 128, 128, seed=seed)
+    note(f"case tiny 128x128 seed {seed}")
+    d = make_workload(w)
+    out = run_contiguous(d)
+    torch.cuda.synchronize()
+    mx, mean = errors(out, oracle.attention(d["q"], d["k"], d["v"]))
+    note(f"  max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+RAGGED = [(1, 1), (1, 37), (5, 5), (17, 17), (63, 100), (64, 64), (65, 300), (130, 1000),
+          (200, 777), (300, 300), (512, 512), (97, 2113)]
+
+
+@pytest.mark.parametrize("q_len,kv_len", RAGGED)
+def test_ragged_contiguous_full(q_len, kv_len):
+    note(f"case contiguous {q_len}x{kv_len}")
+    q, k, v, _ = make_qkv(q_len, kv_len, seed=1000 + q_len + kv_len)
+    out = gqa.gqa_attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    mx, mean = errors(out, oracle.attention(q, k, v))
+    note(f"  max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+@pytest.mark.parametrize("q_len,kv_len,num_blocks", [(1, 16, 1), (33, 70, 9), (64, 257, 40),
+                                                    (100, 1000, 70)])
+def test_paged_full_and_bitwise_equal_to_contiguous(q_len, kv_len, num_blocks):
+    note(f"case paged {q_len}x{kv_len} blocks {num_blocks}")
+    q, k, v, rng = make_qkv(q_len, kv_len, seed=2000 + kv_len)
+    bt = block_table_for(rng, kv_len, num_blocks)
+    kc, vc = scatter_paged(k, bt, num_blocks), scatter_paged(v, bt, num_blocks)
+    out = gqa.gqa_attn_prefill(q.to(DEV), kc.to(DEV), vc.to(DEV), block_table=bt.to(DEV),
+                               kv_len=kv_len)
+    ref_contig = gqa.gqa_attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    mx, mean = errors(out, oracle.attention(q, oracle.gather_paged(kc, bt, kv_len),
+                                            oracle.gather_paged(vc, bt, kv_len)))
+    note(f"  max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+    assert torch.equal(out, ref_contig)
+
+
+@pytest.mark.parametrize("q_len,kv_len", [(1, 1), (7, 50), (64, 64), (100, 333), (300, 1300)])
+def test_int8k_full(q_len, kv_len):
+    note(f"case int8k {q_len}x{kv_len}")
+    q, k, v, _ = make_qkv(q_len, kv_len, seed=3000 + kv_len)
+    kq, ks = oracle.quantize_rows_int8(k)
+    out = gqa.gqa_attn_prefill(q.to(DEV), torch.from_numpy(kq).to(DEV), v.to(DEV),
+                               k_scale=torch.from_numpy(ks).to(DEV))
+    torch.cuda.synchronize()
+    mx, mean = errors(out, oracle.attention_int8k(q, kq, ks, v))
+    note(f"  max {mx:.3e} mean {mean:.3e}")
+    assert mx <= INT8_MAX
+
+
+def test_int8k_zero_query_rows():
+    note("case int8k zero query rows")
+    q, k, v, _ = make_qkv(40, 90, seed=3100)
+    q[5] = 0
+    q[:, 7] = 0
+    kq, ks = oracle.quantize_rows_int8(k)
+    out = gqa.gqa_attn_prefill(q.to(DEV), torch.from_numpy(kq).to(DEV), v.to(DEV),
+                               k_scale=torch.from_numpy(ks).to(DEV))
+    torch.cuda.synchronize()
+    mx, _ = errors(out, oracle.attention_int8k(q, kq, ks, v))
+    assert mx <= INT8_MAX
+
+
+def test_quantizer_bit_exact():
+    note("case quantizer")
+    rng = np.random.default_rng(7)
+    x = torch.from_numpy(rng.standard_normal((1000, 256), dtype=np.float32)
+                         * rng.uniform(1e-3, 100, (1000, 1)).astype(np.float32)).to(torch.bfloat16)
+    x[3] = 0
+    x[4, :] = 0
+    x[4, 0] = 127.0
+    x[4, 1] = 63.5
+    x[4, 2] = -0.5
+    x[4, 3] = 2.5
+    xq, s = gqa.gqa_quantize_rows_int8(x.to(DEV))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_rows_int8(x)
+    np.testing.assert_array_equal(xq.cpu().numpy(), rq)
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+
+
+# ------------------------------------------------------------------ properties
+
+def test_constant_v_is_exact():
+    note("case constant V")
+    q, k, _, _ = make_qkv(96, 400, seed=11)
+    c = torch.randn(4, 256).to(torch.bfloat16)
+    v = c[None].expand(400, 4, 256).contiguous()
+    out = gqa.gqa_attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    want = c.repeat_interleave(6, dim=0)[None].expand(96, 24, 256)
+    assert torch.equal(out.cpu(), want)
+
+
+def test_deterministic():
+    note("case determinism")
+    q, k, v, _ = make_qkv(256, 3000, seed=12)
+    a = gqa.gqa_attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV))
+    b = gqa.gqa_attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_zero_queries_via_binding():
+    q = torch.empty(0, 24, 256, dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros(10, 4, 256, dtype=torch.bfloat16, device=DEV)
+    out = gqa.gqa_attn_prefill(q, k, k)
+    assert out.shape == (0, 24, 256)
+
+
+def test_writes_only_out():
+    """The output buffer is fully overwritten and nothing around it is touched."""
+    note("case output bounds")
+    q, k, v, _ = make_qkv(33, 80, seed=13)
+    buf = torch.full((33 * 24 * 256 + 2 * 4096,), 7.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[4096:4096 + 33 * 24 * 256].view(33, 24, 256)
+    gqa.gqa_attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:4096] == 7.0) and torch.all(buf[-4096:] == 7.0)
+    mx, mean = errors(out, oracle.attention(q, k, v))
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled rows
+
+@pytest.mark.parametrize("idx", [2, 3, 6])
+def test_full_size_contiguous_sampled(idx):
+    w = WORKLOADS[idx]
+    note(f"case {w.name}: generating inputs")
+    d = make_workload(w)
+    note(f"case {w.name}: running")
+    out = run_contiguous(d)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.q_len, seed=idx)
+    ref = oracle.attention(d["q"], d["k"], d["v"], rows=rows)
+    mx, mean = errors(out[torch.from_numpy(rows).to(DEV)], ref)
+    note(f"  {len(rows)} rows: max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+def test_full_size_paged_sampled():
+    w = WORKLOADS[4]
+    note(f"case {w.name}: generating inputs")
+    d = make_workload(w)
+    note(f"case {w.name}: running")
+    out = gqa.gqa_attn_prefill(d["q"].to(DEV), d["k_cache"].to(DEV), d["v_cache"].to(DEV),
+                               block_table=d["block_table"].to(DEV), kv_len=w.kv_len)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.q_len, seed=4)
+    kk = oracle.gather_paged(d["k_cache"], d["block_table"], w.kv_len)
+    vv = oracle.gather_paged(d["v_cache"], d["block_table"], w.kv_len)
+    ref = oracle.attention(d["q"], kk, vv, rows=rows)
+    mx, mean = errors(out[torch.from_numpy(rows).to(DEV)], ref)
+    note(f"  {len(rows)} rows: max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+def test_full_size_int8k_sampled():
+    w = WORKLOADS[5]
+    note(f"case {w.name}: generating inputs")
+    d = make_workload(w)
+    kq, ks = oracle.quantize_rows_int8(d["k"])
+    # the library's quantiser agrees bit for bit with the oracle's on this K
+    gq, gs = gqa.gqa_quantize_rows_int8(d["k"].to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(gq.cpu().numpy(), kq) and np.array_equal(gs.cpu().numpy(), ks)
+    note(f"case {w.name}: running")
+    out = gqa.gqa_attn_prefill(d["q"].to(DEV), gq, d["v"].to(DEV), k_scale=gs)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.q_len, seed=5)
+    ref = oracle.attention_int8k(d["q"], kq, ks, d["v"], rows=rows)
+    mx, _ = errors(out[torch.from_numpy(rows).to(DEV)], ref)
+    note(f"  {len(rows)} rows: max {mx:.3e}")
+    assert mx <= INT8_MAX
+
+
+def test_long_kv_edge():
+    note("case q 64 x kv 131072")
+    q, k, v, _ = make_qkv(64, 131072, seed=21)
+    out = gqa.gqa_attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 31, 32, 62, 63])
+    mx, mean = errors(out[torch.from_numpy(rows).to(DEV)], oracle.attention(q, k, v, rows=rows))
+    note(f"  max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
