@@ -40,7 +40,7 @@ def parse():
                     help="1 tiny, 2 4096x8192, 3 4096x32768 (default), 4 paged 512x32768, "
                          "5 int8-k 3072x16384, 6 4096x16384")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256,
+    ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="query rows of the workload the CPU oracle computes (all 24 heads)")
     return ap.parse_args()
 
