@@ -12,36 +12,42 @@
 // int32(Qq·Kq)·sQ·sK/16), applied to V of KV head h/6, accumulated in FP32 and
 // written as bf16.
 //
-// Work decomposition (one design for gfx950, not the pages' Triton tiling):
-//   * one workgroup = 4 wave64s = one KV head g x a pair of its query heads x
-//     64 query tokens (128 query rows), so every K/V tile staged in LDS serves
-//     128 rows of the GQA group ([DCU report §2, §4]: a program covers tokens x
-//     heads of one group and the reuse of each K/V tile grows with the rows per
-//     program). The three head pairs of a group are three workgroups;
-//   * each wave owns 16 tokens x 2 heads = 32 rows, as two 16-column blocks of
-//     the 16x16 MFMA output (block b = head, column c = token); scores are
-//     computed transposed (S^T = K·Q^T) so every lane holds keys of ONE query
-//     column and the softmax reductions are mostly lane-local;
-//   * the loop walks KV tiles of 32 keys; K is staged row-major with an XOR
-//     swizzle, V is staged transposed (V^T) so it can feed the A operand of the
-//     P·V MFMA, both double-buffered through registers;
+// Work decomposition (designed for gfx950, not the pages' Triton tiling):
+//   * a workgroup is 4 wave64s (one per SIMD) sharing one KV head g; every K/V
+//     tile staged in LDS serves all its query rows ([DCU report §2, §4]: a
+//     program covers tokens x heads of one GQA group, and the reuse of each K/V
+//     tile grows with the rows per program). Each wave owns QB 16-column blocks
+//     of the 16x16 MFMA output: block b = one query head, column c = one token
+//     of a 16-token run. QB = 3: a workgroup is 32 tokens x all 6 heads of g
+//     (192 rows); QB = 2: 64 tokens x a pair of g's heads (128 rows);
+//   * scores are computed transposed (S^T = K·Q^T) so every lane holds keys of
+//     ONE query column: the row maxima need two permlane swaps, and the lane's
+//     S^T registers are directly the P^T operand of the P·V MFMA;
+//   * KV tiles of 64 keys arrive by global_load_lds_dwordx4 (no staging
+//     registers), double-buffered, stored chunk-major ([16-byte chunk][key]) so
+//     that K fragments are one conflict-free ds_read_b128 and the V^T operand of
+//     P·V is two ds_read_b64_tr_b16 transposing reads, all at immediate offsets;
 //   * online softmax in the exp2 domain with a lazy rescale: the running max
 //     used for the exponentials only moves when a tile raises it by more than
 //     2^8, which keeps every exponent <= 2^8 and skips almost every rescale of
-//     the 192 accumulator registers (the result is the same softmax);
+//     the accumulator registers (the result is the same softmax);
 //   * P is rounded to bf16 for the MFMA and the row sums use the rounded values.
 //     Workgroups whose first query sees fewer than 256 keys (short histories,
 //     where few keys carry large weights) multiply with P split into a bf16
-//     high part and a bf16 low part, keeping ~16 bits of P.
+//     high part and a bf16 low part, keeping ~16 bits of P;
 //   * with INT8 keys each query row is quantised in the prologue (once per row,
 //     [INT8 QK §4]) and Q·K^T runs on v_mfma_i32_16x16x64_i8; the int32 score is
-//     scaled by sQ·sK·log2(e)/16 per score before the softmax ([INT8 QK §1]).
+//     scaled by sK·sQ·log2(e)/16 per score before the softmax ([INT8 QK §1]).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
 
 #include "gqa_prefill.h"
+
+#ifndef GQA_DEFAULT_QB
+#define GQA_DEFAULT_QB 2
+#endif
 
 namespace {
 
@@ -53,27 +59,26 @@ constexpr int kBs = GQA_BLOCK_SIZE;      // 16
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTokPerWave = 16;                   // x 2 heads = 32 rows per wave
-constexpr int kTokPerWg = kTokPerWave * kWaves;   // 64 tokens per workgroup
-constexpr int kHeadsPerWg = 2;                    // query heads per workgroup
-constexpr int kPairs = kGroup / kHeadsPerWg;      // 3 workgroups per (KV head, token block)
-constexpr int kQB = kHeadsPerWg;                  // 16-column query blocks per wave
-constexpr int kKt = 32;                           // keys per KV tile
+constexpr int kKt = 64;                  // keys per KV tile
 constexpr int kSplitBelow = 256;
 constexpr float kTau = 8.0f;
 constexpr float kLog2eOver16 = 1.4426950408889634f / 16.0f;
 
-// LDS layout (bytes)
-constexpr int kKTileBf16 = kKt * kD * 2;          // 16 KiB
-constexpr int kKTileI8 = kKt * kD;                // 8 KiB
-constexpr int kVTile = kKt * kD * 2;              // 16 KiB (V^T)
-constexpr int kSkTile = kKt * 4;                  // 128 B of key scales
+// LDS tiles are chunk-major: byte (chunk, key) at chunk * kChunkStride + key * 16.
+constexpr int kChunkStride = kKt * 16;               // 1 KiB
+constexpr int kKTileBf16 = (kD * 2 / 16) * kChunkStride;  // 32 chunks: 32 KiB
+constexpr int kKTileI8 = (kD / 16) * kChunkStride;        // 16 chunks: 16 KiB
+constexpr int kVTile = (kD * 2 / 16) * kChunkStride;      // 32 KiB
+constexpr int kSkTile = kKt * 4;                          // 256 B of key scales
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct Params {
   const uint8_t* q;        // bf16 [q_len, 24, 256]
@@ -85,38 +90,73 @@ struct Params {
   int32_t num_blocks;
   int32_t q_len;
   int32_t kv_len;
-  int32_t n_tblk;          // ceil(q_len / 64)
+  int32_t n_tblk;          // token blocks of the grid
+};
+
+// Workgroup shape for QB 16-column query blocks per wave.
+template <int QB>
+struct Shape {
+  static constexpr int kTokenBlocks = (QB == 3) ? 2 : 4;            // 16-token runs per workgroup
+  static constexpr int kHeadGroups = kWaves / kTokenBlocks;         // QB-head groups per workgroup
+  static constexpr int kHeadsPerWg = QB * kHeadGroups;              // 6 or 2
+  static constexpr int kTokPerWg = 16 * kTokenBlocks;               // 32 or 64
+  static constexpr int kSplitsPerGroup = kGroup / kHeadsPerWg;      // 1 or 3 workgroups per (g, tokens)
 };
 
 __device__ __forceinline__ float wave_xor_max(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask));
 }
-
-__device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi_src, lo_src, sel);
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Byte offset of K row chunk (16 B) `chunk` of key `key` inside a staged K tile.
-// XOR swizzle on the low three chunk bits: the 8 lanes of one ds_read_b128 phase
-// read 8 different keys at the same logical chunk and land in 8 different
-// 16-byte bank groups.
-template <int ROW_BYTES>
-__device__ __forceinline__ int k_lds_off(int key, int chunk) {
-  return key * ROW_BYTES + ((chunk ^ (key & 7)) << 4);
+// One V^T operand of the P·V MFMA from a chunk-major V tile: two transposing reads,
+// 16 keys apart (see the lane mapping at the call site). Issued as inline assembly
+// so the compiler does not make them wait for the global->LDS copies into the
+// other buffer; `vt_wait` must run before the registers are used.
+struct VtFrag {
+  uint2 lo, hi;
+};
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-// Byte offset of the 16-byte group `grp` (keys {4grp..4grp+3, 16+4grp..16+4grp+3})
-// of V^T row `d`. Within a row (64 B = the tile's 32 keys of one feature), group
-// grp holds keys 4grp..4grp+3 then 16+4grp..16+4grp+3: exactly the 8 keys one
-// lane feeds to the P·V MFMA, in the order its S^T registers hold them. The
-// group index is XOR-swizzled by (d >> 1) & 3 so the 8 lanes of a read phase
-// (8 consecutive d) hit 8 different bank groups.
-__device__ __forceinline__ int vt_lds_off(int d, int grp) {
-  return d * 64 + ((grp ^ ((d >> 1) & 3)) << 4);
+template <int OFF>
+__device__ __forceinline__ void vt_issue(VtFrag& f, uint32_t addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%3\n\tds_read_b64_tr_b16 %1, %2 offset:%4"
+               : "=v"(f.lo), "=v"(f.hi)
+               : "v"(addr), "i"(OFF), "i"(OFF + 256));
 }
 
+// Wait until at most N LDS operations of this wave are outstanding (LDS operations
+// complete in order), tying the fragment's registers to the wait.
+template <int N>
+__device__ __forceinline__ void vt_wait(VtFrag& f) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(f.lo), "+v"(f.hi) : "i"(N));
+}
+
+__device__ __forceinline__ bf16x8 vt_value(const VtFrag& f) {
+  const uint4 u = make_uint4(f.lo.x, f.lo.y, f.hi.x, f.hi.y);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Element index of the row (key, kv head g) in the K/V arrays.
 template <bool PAGED>
-__device__ __forceinline__ size_t kv_row_elem(const Params& p, int g, int key, int blk) {
+__device__ __forceinline__ size_t kv_row(int g, int key, int blk) {
   if constexpr (PAGED) {
     return ((size_t)(blk * kHkv + g) * kBs + (key & (kBs - 1))) * kD;
   } else {
@@ -124,147 +164,293 @@ __device__ __forceinline__ size_t kv_row_elem(const Params& p, int g, int key, i
   }
 }
 
+__device__ __forceinline__ int clamp_block(const Params& p, int blk) {
+  return min(max(blk, 0), p.num_blocks - 1);
+}
+
+// Issue this wave's share of the global -> LDS copies for the KV tile at kbase.
+// Lane t copies key kbase + t (clamped to the last key: keys past kv_len are
+// finite duplicates that the causal mask hides); each instruction moves one
+// 16-byte chunk column of the 64 keys. `blk` is the lane's physical block
+// (paged caches only).
 template <bool PAGED, bool INT8K>
-struct Stage {
-  uint4 kreg[INT8K ? 2 : 4];
-  uint2 vreg[2][4];
-  float sk;
+__device__ __forceinline__ void issue_tile(const Params& p, int g, int kbase, int w, int lane,
+                                           int blk, uint8_t* kbuf, uint8_t* vbuf, float* skbuf) {
+  const int key = min(kbase + lane, p.kv_len - 1);
+  const size_t row = kv_row<PAGED>(g, key, blk);
+  const uint8_t* krow = p.k + row * (INT8K ? 1 : 2);
+  const uint8_t* vrow = p.v + row * 2;
+  constexpr int kKChunks = INT8K ? kD / 16 : kD * 2 / 16;
+  constexpr int kKPerWave = kKChunks / kWaves;
+#pragma unroll
+  for (int i = 0; i < kKPerWave; ++i) {
+    const int c = w * kKPerWave + i;
+    __builtin_amdgcn_global_load_lds(krow + c * 16, kbuf + c * kChunkStride, 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = w * 8 + i;
+    __builtin_amdgcn_global_load_lds(vrow + c * 16, vbuf + c * kChunkStride, 16, 0, 0);
+  }
+  if constexpr (INT8K) {
+    if (w == 0) __builtin_amdgcn_global_load_lds(p.ks + (size_t)key * kHkv + g, skbuf, 4, 0, 0);
+  }
+}
+
+// Physical block of the lane's key in the tile at kbase (paged caches).
+template <bool PAGED>
+__device__ __forceinline__ int tile_block(const Params& p, int kbase, int lane) {
+  if constexpr (PAGED) {
+    const int key = min(kbase + lane, p.kv_len - 1);
+    return clamp_block(p, p.bt[key >> 4]);
+  } else {
+    return 0;
+  }
+}
+
+__device__ __forceinline__ void wait_vm_all() {
+  // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Step N of O^T += V^T · P^T over a 64-key tile: N = 16 ks + db, ks = 32-key half,
+// db = 16-feature block. Issues the transposing reads of step N + 1, waits for
+// step N's, runs its MFMAs.
+template <int N, int QB, bool SPLIT>
+struct PvStep {
+  static __device__ __forceinline__ void run(VtFrag (&vf)[2], uint32_t vaddr,
+                                             const bf16x8 (&ph)[QB][2], const bf16x8 (&pl)[QB][2],
+                                             f32x4 (&o)[16][QB]) {
+    constexpr int ks = N >> 4, db = N & 15;
+    if constexpr (N + 1 < 32) {
+      constexpr int ks1 = (N + 1) >> 4, db1 = (N + 1) & 15;
+      vt_issue<db1 * 2 * kChunkStride + 32 * ks1 * 16>(vf[(N + 1) & 1], vaddr);
+      vt_wait<2>(vf[N & 1]);
+    } else {
+      vt_wait<0>(vf[N & 1]);
+    }
+    const bf16x8 v = vt_value(vf[N & 1]);
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      o[db][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, ph[b][ks], o[db][b], 0, 0, 0);
+      if constexpr (SPLIT)
+        o[db][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pl[b][ks], o[db][b], 0, 0, 0);
+    }
+    if constexpr (N + 1 < 32) PvStep<N + 1, QB, SPLIT>::run(vf, vaddr, ph, pl, o);
+  }
 };
 
-// Global -> registers for KV tile starting at key `kbase`.
-template <bool PAGED, bool INT8K>
-__device__ __forceinline__ void stage_load(const Params& p, int g, int kbase, int tid,
-                                           Stage<PAGED, INT8K>& st) {
-  int blk0 = 0, blk1 = 0;
-  if constexpr (PAGED) {
-    const int tb = kbase >> 4;
-    blk0 = p.bt[tb];
-    blk1 = (kbase + kBs < p.kv_len) ? p.bt[tb + 1] : blk0;
-    blk0 = min(max(blk0, 0), p.num_blocks - 1);
-    blk1 = min(max(blk1, 0), p.num_blocks - 1);
-  }
-  // K: bf16 rows are 32 chunks of 16 B (4 per thread); int8 rows are 16 chunks (2 per thread)
-  constexpr int kChunks = INT8K ? 16 : 32;
-  constexpr int kShift = INT8K ? 4 : 5;
-  constexpr int kPer = INT8K ? 2 : 4;
-  constexpr int kElem = INT8K ? 1 : 2;
+template <bool PAGED, bool INT8K, int QB>
+struct Tile {
+  // S^T for 64 keys x (QB x 16) columns, P and the running softmax state
+  template <bool SPLIT>
+  static __device__ __forceinline__ void compute(const uint8_t* kbuf, const uint8_t* vbuf,
+                                                 const float* skbuf, int kbase, int L, int c,
+                                                 int lane, bool diag, int limit,
+                                                 const bf16x8 (&qf)[INT8K ? 1 : QB][INT8K ? 1 : 8],
+                                                 const i32x4 (&qq)[INT8K ? QB : 1][INT8K ? 4 : 1],
+                                                 const float (&qs)[QB], float (&m)[QB],
+                                                 float (&l)[QB], f32x4 (&o)[16][QB]) {
+    // ---- S^T = K · Q^T ----
+    float sc[QB][16];   // [query block][key slot 4 kb + r] for key 16 kb + 4 L + r
+    const int koff = L * kChunkStride + c * 16;
+    if constexpr (!INT8K) {
+      f32x4 acc[QB][4];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int u = tid + kThreads * i;
-    const int key = u >> kShift;
-    const int chunk = u & (kChunks - 1);
-    const int kk = kbase + key;
-    if (kk < p.kv_len) {
-      const size_t e = kv_row_elem<PAGED>(p, g, kk, key < kBs ? blk0 : blk1);
-      st.kreg[i] = *reinterpret_cast<const uint4*>(p.k + e * kElem + chunk * 16);
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc[b][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // K fragments for step s + 1 are read while the MFMAs of step s run
+      bf16x8 kf[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        kf[0][kb] = *reinterpret_cast<const bf16x8*>(kbuf + koff + kb * 256);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if (s + 1 < 8) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            kf[(s + 1) & 1][kb] = *reinterpret_cast<const bf16x8*>(
+                kbuf + koff + 4 * (s + 1) * kChunkStride + kb * 256);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int b = 0; b < QB; ++b)
+            acc[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s & 1][kb], qf[b][s], acc[b][kb],
+                                                                 0, 0, 0);
+      }
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[b][4 * kb + r] = acc[b][kb][r] * kLog2eOver16;
     } else {
-      st.kreg[i] = make_uint4(0, 0, 0, 0);
-    }
-  }
-  // V: 2 units of 4 keys x 4 features per thread
+      i32x4 acc[QB][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int kq = tid & 7;
-    const int dq = (tid >> 3) + 32 * i;
+      for (int b = 0; b < QB; ++b)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = 4 * kq + r;
-      const int kk = kbase + key;
-      if (kk < p.kv_len) {
-        const size_t e = kv_row_elem<PAGED>(p, g, kk, key < kBs ? blk0 : blk1);
-        st.vreg[i][r] = *reinterpret_cast<const uint2*>(p.v + (e + 4 * dq) * 2);
-      } else {
-        st.vreg[i][r] = make_uint2(0, 0);
+        for (int kb = 0; kb < 4; ++kb) acc[b][kb] = i32x4{0, 0, 0, 0};
+      i32x4 kf[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        kf[0][kb] = *reinterpret_cast<const i32x4*>(kbuf + koff + kb * 256);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (s + 1 < 4) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            kf[(s + 1) & 1][kb] = *reinterpret_cast<const i32x4*>(
+                kbuf + koff + 4 * (s + 1) * kChunkStride + kb * 256);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int b = 0; b < QB; ++b)
+            acc[b][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf[s & 1][kb], qq[b][s], acc[b][kb],
+                                                               0, 0, 0);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const f32x4 sk = *reinterpret_cast<const f32x4*>(skbuf + 16 * kb + 4 * L);
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[b][4 * kb + r] = (float)acc[b][kb][r] * sk[r] * qs[b];
       }
     }
-  }
-  if constexpr (INT8K) {
-    st.sk = 0.0f;
-    if (tid < kKt && kbase + tid < p.kv_len) st.sk = p.ks[(size_t)(kbase + tid) * kHkv + g];
-  }
-}
 
-// Registers -> LDS (K swizzled, V transposed).
-template <bool PAGED, bool INT8K>
-__device__ __forceinline__ void stage_store(uint8_t* kbuf, uint8_t* vtbuf, float* skbuf, int tid,
-                                            const Stage<PAGED, INT8K>& st) {
-  constexpr int kChunks = INT8K ? 16 : 32;
-  constexpr int kShift = INT8K ? 4 : 5;
-  constexpr int kPer = INT8K ? 2 : 4;
-  constexpr int kRow = INT8K ? kD : 2 * kD;
+    // ---- causal mask (only tiles that reach past the workgroup's first query) ----
+    if (diag) {
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int u = tid + kThreads * i;
-    const int key = u >> kShift;
-    const int chunk = u & (kChunks - 1);
-    *reinterpret_cast<uint4*>(kbuf + k_lds_off<kRow>(key, chunk)) = st.kreg[i];
-  }
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int kq = tid & 7;
-    const int dq = (tid >> 3) + 32 * i;
-    const int grp = kq & 3;
-    const int half = kq >> 2;
-    const uint2* r = st.vreg[i];
-    // 4x4 transpose of bf16: row r = key 4kq+r holding features 4dq..4dq+3
-    uint2 col[4];
-    col[0] = make_uint2(perm_b32(r[1].x, r[0].x, 0x05040100u), perm_b32(r[3].x, r[2].x, 0x05040100u));
-    col[1] = make_uint2(perm_b32(r[1].x, r[0].x, 0x07060302u), perm_b32(r[3].x, r[2].x, 0x07060302u));
-    col[2] = make_uint2(perm_b32(r[1].y, r[0].y, 0x05040100u), perm_b32(r[3].y, r[2].y, 0x05040100u));
-    col[3] = make_uint2(perm_b32(r[1].y, r[0].y, 0x07060302u), perm_b32(r[3].y, r[2].y, 0x07060302u));
+        for (int r = 0; r < 4; ++r) {
+          const int key = kbase + 16 * kb + 4 * L + r;
+          if (key > limit) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = 4 * dq + j;
-      *reinterpret_cast<uint2*>(vtbuf + vt_lds_off(d, grp) + half * 8) = col[j];
+            for (int b = 0; b < QB; ++b) sc[b][4 * kb + r] = -__builtin_inff();
+          }
+        }
     }
+
+    // ---- online softmax (exp2 domain, lazy rescale) ----
+    float mnew[QB];
+    bool need = false;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      float mx = sc[b][0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[b][e]);
+      mx = xor16_max(mx);
+      mx = xor32_max(mx);
+      mnew[b] = fmaxf(m[b], mx);
+      need = need || (mnew[b] > m[b] + kTau);
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        const float alpha = __builtin_amdgcn_exp2f(m[b] - mnew[b]);
+        m[b] = mnew[b];
+        l[b] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 16; ++db) o[db][b] *= alpha;
+      }
+    }
+    // P^T operands: k-step ks covers keys 32 ks .. 32 ks + 31; a lane's 8 elements are
+    // keys 32 ks + 4 L + {0..3} and 32 ks + 16 + 4 L + {0..3} = its S^T slots 8 ks .. 8 ks + 7
+    bf16x8 ph[QB][2], pl[QB][2];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        f32x8 pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(sc[b][8 * ks + e] - m[b]);
+        ph[b][ks] = __builtin_convertvector(pv, bf16x8);
+        const f32x8 hi = __builtin_convertvector(ph[b][ks], f32x8);
+        if constexpr (SPLIT) {
+          pl[b][ks] = __builtin_convertvector(pv - hi, bf16x8);
+          const f32x8 lo = __builtin_convertvector(pl[b][ks], f32x8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sum += hi[e] + lo[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sum += hi[e];
+        }
+      }
+      l[b] += sum;
+    }
+
+    // ---- O^T += V^T · P^T ----
+    // transposing read: lane i of 16-lane group L fetches features 16 db + 4 (i & 3) .. +3 of
+    // key 32 ks + 16 h + 4 L + (i >> 2); after the transpose lane (L, c) holds
+    // V[32 ks + 16 h + 4 L + k][16 db + c] for k = 0..3
+    const int voff = ((c & 3) >> 1) * kChunkStride + (4 * L + (c >> 2)) * 16 + 8 * (c & 1);
+    // V^T fragments for step n + 1 (n = 16 ks + db) are read while the MFMAs of step n run
+    VtFrag vf[2];
+    const uint32_t vaddr = lds_addr(vbuf) + voff;
+    vt_issue<0>(vf[0], vaddr);
+    PvStep<0, QB, SPLIT>::run(vf, vaddr, ph, pl, o);
   }
-  if constexpr (INT8K) {
-    if (tid < kKt) skbuf[tid] = st.sk;
-  }
+};
+
+template <bool PAGED, bool INT8K, int QB>
+constexpr int stage_bytes() {
+  return (INT8K ? kKTileI8 : kKTileBf16) + kVTile + (INT8K ? kSkTile : 0);
 }
 
-template <bool PAGED, bool INT8K>
-__global__ __launch_bounds__(kThreads, 1) void gqa_prefill_kernel(const Params p) {
+// The whole workgroup program. SPLIT selects the P·V form (see the file header); it
+// is fixed per workgroup, so each form is a separate straight-line program.
+template <bool PAGED, bool INT8K, int QB, bool SPLIT>
+__device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
+  using S = Shape<QB>;
   constexpr int kKTile = INT8K ? kKTileI8 : kKTileBf16;
-  constexpr int kSk = INT8K ? kSkTile : 0;
-  constexpr int kStage = kKTile + kVTile + kSk;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  constexpr int kStage = stage_bytes<PAGED, INT8K, QB>();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int L = lane >> 4;      // k-group of the MFMA operands / row group of the output
   const int c = lane & 15;      // query column (token) inside a 16-column block
+  const int tw = w % S::kTokenBlocks;
+  const int hw = w / S::kTokenBlocks;
 
-  // Workgroup id -> (KV head, head pair, token block). id % 4 is the KV head, so
-  // workgroups dispatched round-robin over the 8 XCDs keep one KV head per XCD
-  // (its K/V stream shares that XCD's L2); token blocks go longest first.
+  // Workgroup id -> (KV head, head subset, token block). id % 4 is the KV head, so
+  // workgroups dispatched round-robin over the 8 XCDs keep one KV head per XCD (its
+  // K/V stream shares that XCD's L2); token blocks go longest first.
   const int id = blockIdx.x;
   const int g = id & (kHkv - 1);
   const int rest = id >> 2;
-  const int hp = rest % kPairs;
-  const int tblk = p.n_tblk - 1 - rest / kPairs;
-  const int t0 = tblk * kTokPerWg;
+  const int hsel = rest % S::kSplitsPerGroup;
+  const int tblk = p.n_tblk - 1 - rest / S::kSplitsPerGroup;
+  const int t0 = tblk * S::kTokPerWg;
   const int off = p.kv_len - p.q_len;
+  const int head0 = kGroup * g + hsel * S::kHeadsPerWg + hw * QB;   // head of query block 0
 
-  // query column (b, c) of this lane: token t0 + 16w + c, head 6g + 2hp + b
-  const int tok = t0 + kTokPerWave * w + c;
+  // query column (b, c) of this lane: token t0 + 16 tw + c, head head0 + b
+  const int tok = t0 + 16 * tw + c;
   const bool tok_ok = tok < p.q_len;
   const int limit = off + tok;   // last visible key of this column
 
-  const int last_tok = min(t0 + kTokPerWg, p.q_len);
-  const int n_keys = off + last_tok;
-  const int ntiles = (n_keys + kKt - 1) / kKt;
-  const bool split = (off + t0 + 1) < kSplitBelow;
+  const int last_tok = min(t0 + S::kTokPerWg, p.q_len);
+  const int ntiles = (off + last_tok + kKt - 1) / kKt;
+
+  // start the first tile's copies before the Q prologue
+  int blk = tile_block<PAGED>(p, 0, lane);
+  issue_tile<PAGED, INT8K>(p, g, 0, w, lane, blk, smem, smem + kKTile,
+                           reinterpret_cast<float*>(smem + kKTile + kVTile));
+  if (ntiles > 1) blk = tile_block<PAGED>(p, kKt, lane);
 
   // ---- prologue: Q fragments (B operand of S^T = K·Q^T) ----
-  bf16x8 qf[INT8K ? 1 : kQB][INT8K ? 1 : 8];
-  i32x4 qq[INT8K ? kQB : 1][INT8K ? 4 : 1];
-  float qs[kQB];
+  bf16x8 qf[INT8K ? 1 : QB][INT8K ? 1 : 8];
+  i32x4 qq[INT8K ? QB : 1][INT8K ? 4 : 1];
+  float qs[QB];
 #pragma unroll
-  for (int b = 0; b < kQB; ++b) {
-    const int head = kGroup * g + kHeadsPerWg * hp + b;
-    const uint8_t* qrow = p.q + ((size_t)tok * kHq + head) * kD * 2;
+  for (int b = 0; b < QB; ++b) {
+    const uint8_t* qrow = p.q + ((size_t)tok * kHq + head0 + b) * kD * 2;
     if constexpr (!INT8K) {
       qs[b] = kLog2eOver16;
 #pragma unroll
@@ -274,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void gqa_prefill_kernel(const Params p
         qf[b][s] = __builtin_bit_cast(bf16x8, raw);
       }
     } else {
-      // each lane holds features 64s + 16L .. +15 (s = 0..3) of its query row;
+      // each lane holds features 64 s + 16 L .. +15 (s = 0..3) of its query row;
       // the four lanes L = 0..3 of column c hold the whole row
       float x[4][16];
       float amax = 0.0f;
@@ -292,8 +478,8 @@ __global__ __launch_bounds__(kThreads, 1) void gqa_prefill_kernel(const Params p
           }
         }
       }
-      amax = wave_xor_max(amax, 16);
-      amax = wave_xor_max(amax, 32);
+      amax = xor16_max(amax);
+      amax = xor32_max(amax);
       const float sq = amax / 127.0f;
       qs[b] = sq * kLog2eOver16;
 #pragma unroll
@@ -316,176 +502,44 @@ __global__ __launch_bounds__(kThreads, 1) void gqa_prefill_kernel(const Params p
   }
 
   // ---- accumulators: O^T blocks [feature block db][query block b] ----
-  f32x4 o[16][kQB];
+  f32x4 o[16][QB];
 #pragma unroll
   for (int db = 0; db < 16; ++db)
 #pragma unroll
-    for (int b = 0; b < kQB; ++b) o[db][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[kQB], l[kQB];
+    for (int b = 0; b < QB; ++b) o[db][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[QB], l[QB];
 #pragma unroll
-  for (int b = 0; b < kQB; ++b) {
+  for (int b = 0; b < QB; ++b) {
     m[b] = -__builtin_inff();
     l[b] = 0.0f;
   }
 
-  // ---- first tile ----
-  Stage<PAGED, INT8K> st;
-  stage_load<PAGED, INT8K>(p, g, 0, tid, st);
-  stage_store<PAGED, INT8K>(smem, smem + kKTile, reinterpret_cast<float*>(smem + kKTile + kVTile),
-                            tid, st);
-  __syncthreads();
-
+  using T = Tile<PAGED, INT8K, QB>;
   for (int j = 0; j < ntiles; ++j) {
     const int kbase = j * kKt;
-    uint8_t* kbuf = smem + (j & 1) * kStage;
-    uint8_t* vtbuf = kbuf + kKTile;
-    const float* skbuf = reinterpret_cast<const float*>(vtbuf + kVTile);
-    const bool more = (j + 1) < ntiles;
-    if (more) stage_load<PAGED, INT8K>(p, g, kbase + kKt, tid, st);
-
-    // ---- S^T = K · Q^T for 32 keys x 32 query columns ----
-    float sc[kQB][8];   // [query block][key slot: 4 keys of block kb=0, then 4 of kb=1]
-    if constexpr (!INT8K) {
-      f32x4 acc[kQB][2];
-#pragma unroll
-      for (int b = 0; b < kQB; ++b) acc[b][0] = acc[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-              kbuf + k_lds_off<2 * kD>(16 * kb + c, 4 * s + L));
-#pragma unroll
-          for (int b = 0; b < kQB; ++b)
-            acc[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[b][s], acc[b][kb], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < kQB; ++b)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[b][4 * kb + r] = acc[b][kb][r] * kLog2eOver16;
-    } else {
-      i32x4 acc[kQB][2];
-#pragma unroll
-      for (int b = 0; b < kQB; ++b) acc[b][0] = acc[b][1] = i32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const i32x4 kf = *reinterpret_cast<const i32x4*>(
-              kbuf + k_lds_off<kD>(16 * kb + c, 4 * s + L));
-#pragma unroll
-          for (int b = 0; b < kQB; ++b)
-            acc[b][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf, qq[b][s], acc[b][kb], 0, 0, 0);
-        }
-      }
-      const f32x4 sk0 = *reinterpret_cast<const f32x4*>(skbuf + 4 * L);
-      const f32x4 sk1 = *reinterpret_cast<const f32x4*>(skbuf + 16 + 4 * L);
-#pragma unroll
-      for (int b = 0; b < kQB; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sc[b][r] = (float)acc[b][0][r] * sk0[r] * qs[b];
-          sc[b][4 + r] = (float)acc[b][1][r] * sk1[r] * qs[b];
-        }
+    uint8_t* cur = smem + (j & 1) * kStage;
+    uint8_t* nxt = smem + ((j + 1) & 1) * kStage;
+    wait_vm_all();
+    __syncthreads();   // tile j is in `cur`; everyone is done with `nxt` (tile j - 1)
+    if (j + 1 < ntiles) {
+      issue_tile<PAGED, INT8K>(p, g, kbase + kKt, w, lane, blk, nxt, nxt + kKTile,
+                               reinterpret_cast<float*>(nxt + kKTile + kVTile));
+      if (j + 2 < ntiles) blk = tile_block<PAGED>(p, kbase + 2 * kKt, lane);
     }
-
-    // ---- causal mask (only tiles that reach past the workgroup's first query) ----
-    if (kbase + kKt - 1 > off + t0) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kbase + 16 * kb + 4 * L + r;
-          if (key > limit) {
-#pragma unroll
-            for (int b = 0; b < kQB; ++b) sc[b][4 * kb + r] = -__builtin_inff();
-          }
-        }
-    }
-
-    // ---- online softmax (exp2 domain, lazy rescale) ----
-    float mnew[kQB];
-    bool need = false;
-#pragma unroll
-    for (int b = 0; b < kQB; ++b) {
-      float mx = sc[b][0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[b][e]);
-      mx = wave_xor_max(mx, 16);
-      mx = wave_xor_max(mx, 32);
-      mnew[b] = fmaxf(m[b], mx);
-      need = need || (mnew[b] > m[b] + kTau);
-    }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int b = 0; b < kQB; ++b) {
-        const float alpha = __builtin_amdgcn_exp2f(m[b] - mnew[b]);
-        m[b] = mnew[b];
-        l[b] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 16; ++db) o[db][b] *= alpha;
-      }
-    }
-    bf16x8 ph[kQB], pl[kQB];
-#pragma unroll
-    for (int b = 0; b < kQB; ++b) {
-      f32x8 pv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(sc[b][e] - m[b]);
-      ph[b] = __builtin_convertvector(pv, bf16x8);
-      const f32x8 hi = __builtin_convertvector(ph[b], f32x8);
-      float sum = 0.0f;
-      if (split) {
-        pl[b] = __builtin_convertvector(pv - hi, bf16x8);
-        const f32x8 lo = __builtin_convertvector(pl[b], f32x8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sum += hi[e] + lo[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sum += hi[e];
-      }
-      l[b] += sum;
-    }
-
-    // ---- O^T += V^T · P^T ----
-#pragma unroll
-    for (int db = 0; db < 16; ++db) {
-      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vtbuf + vt_lds_off(16 * db + c, L));
-#pragma unroll
-      for (int b = 0; b < kQB; ++b)
-        o[db][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, ph[b], o[db][b], 0, 0, 0);
-    }
-    if (split) {
-#pragma unroll
-      for (int db = 0; db < 16; ++db) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vtbuf + vt_lds_off(16 * db + c, L));
-#pragma unroll
-        for (int b = 0; b < kQB; ++b)
-          o[db][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[b], o[db][b], 0, 0, 0);
-      }
-    }
-
-    if (more) {
-      uint8_t* nk = smem + ((j + 1) & 1) * kStage;
-      stage_store<PAGED, INT8K>(nk, nk + kKTile, reinterpret_cast<float*>(nk + kKTile + kVTile),
-                                tid, st);
-    }
-    __syncthreads();
+    T::template compute<SPLIT>(cur, cur + kKTile, reinterpret_cast<const float*>(cur + kKTile + kVTile),
+                               kbase, L, c, lane, kbase + kKt - 1 > off + t0, limit, qf, qq, qs, m,
+                               l, o);
   }
 
   // ---- epilogue: O / l -> bf16 ----
 #pragma unroll
-  for (int b = 0; b < kQB; ++b) {
+  for (int b = 0; b < QB; ++b) {
     float lt = l[b];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    lt = xor16_sum(lt);
+    lt = xor32_sum(lt);
     const float inv = 1.0f / lt;
     if (tok_ok) {
-      const int head = kGroup * g + kHeadsPerWg * hp + b;
-      uint8_t* orow = p.out + ((size_t)tok * kHq + head) * kD * 2;
+      uint8_t* orow = p.out + ((size_t)tok * kHq + head0 + b) * kD * 2;
 #pragma unroll
       for (int db = 0; db < 16; ++db) {
         const f32x4 y = o[db][b] * inv;
@@ -494,6 +548,18 @@ __global__ __launch_bounds__(kThreads, 1) void gqa_prefill_kernel(const Params p
       }
     }
   }
+}
+
+template <bool PAGED, bool INT8K, int QB>
+__global__ __launch_bounds__(kThreads, 1) void gqa_prefill_kernel(const Params p) {
+  using S = Shape<QB>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * stage_bytes<PAGED, INT8K, QB>()];
+  const int rest = blockIdx.x >> 2;
+  const int t0 = (p.n_tblk - 1 - rest / S::kSplitsPerGroup) * S::kTokPerWg;
+  if (p.kv_len - p.q_len + t0 + 1 < kSplitBelow)
+    run<PAGED, INT8K, QB, true>(p, smem);
+  else
+    run<PAGED, INT8K, QB, false>(p, smem);
 }
 
 // ---- standalone row quantiser: one wave per 256-element row ----
@@ -536,22 +602,39 @@ int check_prefill_lengths(int32_t q_len, int32_t kv_len) {
 
 struct Launch {
   const char* name;
+  int qb;
+  int n_tblk;
   int workgroups;
   int threads;
   int lds_bytes;
 };
 
-Launch plan_for(int32_t q_len, int32_t kv_len, bool paged, bool int8k) {
-  (void)kv_len;
-  const int n_tblk = (q_len + kTokPerWg - 1) / kTokPerWg;
+constexpr int kDefaultQB = GQA_DEFAULT_QB;
+
+template <int QB>
+Launch shape_launch(int32_t q_len, bool int8k) {
+  using S = Shape<QB>;
+  const int n_tblk = (q_len + S::kTokPerWg - 1) / S::kTokPerWg;
   Launch lc;
-  lc.workgroups = n_tblk * kHkv * kPairs;
+  lc.qb = QB;
+  lc.n_tblk = n_tblk;
+  lc.workgroups = n_tblk * kHkv * S::kSplitsPerGroup;
   lc.threads = kThreads;
   lc.lds_bytes = 2 * ((int8k ? kKTileI8 : kKTileBf16) + kVTile + (int8k ? kSkTile : 0));
+  return lc;
+}
+
+// Dispatch rule (the analogue of the pages' q_len/kv_len-gated variant choice): one
+// kernel family; the query-block count per wave is the only shape parameter.
+Launch plan_for(int32_t q_len, int32_t kv_len, bool paged, bool int8k) {
+  (void)kv_len;
+  Launch lc = shape_launch<kDefaultQB>(q_len, int8k);
   if (int8k)
-    lc.name = "int8k_contiguous_t64h2_kt32";
+    lc.name = kDefaultQB == 3 ? "int8k_contiguous_t32h6_kt64" : "int8k_contiguous_t64h2_kt64";
+  else if (paged)
+    lc.name = kDefaultQB == 3 ? "bf16_paged_t32h6_kt64" : "bf16_paged_t64h2_kt64";
   else
-    lc.name = paged ? "bf16_paged_t64h2_kt32" : "bf16_contiguous_t64h2_kt32";
+    lc.name = kDefaultQB == 3 ? "bf16_contiguous_t32h6_kt64" : "bf16_contiguous_t64h2_kt64";
   return lc;
 }
 
@@ -616,17 +699,17 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, const int32_t*
   p.num_blocks = paged ? num_blocks : 0;
   p.q_len = q_len;
   p.kv_len = kv_len;
-  p.n_tblk = (q_len + kTokPerWg - 1) / kTokPerWg;
 
   const Launch lc = plan_for(q_len, kv_len, paged, int8k);
+  p.n_tblk = lc.n_tblk;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(lc.workgroups), block(lc.threads);
   if (int8k)
-    hipLaunchKernelGGL((gqa_prefill_kernel<false, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gqa_prefill_kernel<false, true, kDefaultQB>), grid, block, 0, s, p);
   else if (paged)
-    hipLaunchKernelGGL((gqa_prefill_kernel<true, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gqa_prefill_kernel<true, false, kDefaultQB>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((gqa_prefill_kernel<false, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gqa_prefill_kernel<false, false, kDefaultQB>), grid, block, 0, s, p);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
