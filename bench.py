@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="query rows of the workload the CPU oracle computes (all 24 heads)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="before warm-up, run a plain device copy of MIB MiB (for scaling "
+                         "HBM counters by a kernel whose traffic is known)")
     return ap.parse_args()
 
 
@@ -121,6 +124,16 @@ def main():
     def step():
         gqa.gqa_attn_prefill(q, k, v, out=out, stream=stream, **kw)
 
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"bench: copied {n} bytes twice for counter calibration", file=sys.stderr, flush=True)
+        del src, dst
     print(f"bench: {w.name} warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()

@@ -43,6 +43,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <type_traits>
+
 #include "gqa_prefill.h"
 
 #ifndef GQA_DEFAULT_QB
@@ -64,18 +66,14 @@ constexpr int kSplitBelow = 256;
 constexpr float kTau = 8.0f;
 constexpr float kLog2eOver16 = 1.4426950408889634f / 16.0f;
 
-// LDS tiles are chunk-major: byte (chunk, key) at chunk * kChunkStride + key * 16.
-constexpr int kChunkStride = kKt * 16;               // 1 KiB
-constexpr int kKTileBf16 = (kD * 2 / 16) * kChunkStride;  // 32 chunks: 32 KiB
-constexpr int kKTileI8 = (kD / 16) * kChunkStride;        // 16 chunks: 16 KiB
-constexpr int kVTile = (kD * 2 / 16) * kChunkStride;      // 32 KiB
-constexpr int kSkTile = kKt * 4;                          // 256 B of key scales
+constexpr int kSkTile = kKt * 4;         // 256 B of key scales per tile
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -123,37 +121,6 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One V^T operand of the P·V MFMA from a chunk-major V tile: two transposing reads,
-// 16 keys apart (see the lane mapping at the call site). Issued as inline assembly
-// so the compiler does not make them wait for the global->LDS copies into the
-// other buffer; `vt_wait` must run before the registers are used.
-struct VtFrag {
-  uint2 lo, hi;
-};
-
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
-}
-
-template <int OFF>
-__device__ __forceinline__ void vt_issue(VtFrag& f, uint32_t addr) {
-  asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%3\n\tds_read_b64_tr_b16 %1, %2 offset:%4"
-               : "=v"(f.lo), "=v"(f.hi)
-               : "v"(addr), "i"(OFF), "i"(OFF + 256));
-}
-
-// Wait until at most N LDS operations of this wave are outstanding (LDS operations
-// complete in order), tying the fragment's registers to the wait.
-template <int N>
-__device__ __forceinline__ void vt_wait(VtFrag& f) {
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(f.lo), "+v"(f.hi) : "i"(N));
-}
-
-__device__ __forceinline__ bf16x8 vt_value(const VtFrag& f) {
-  const uint4 u = make_uint4(f.lo.x, f.lo.y, f.hi.x, f.hi.y);
-  return __builtin_bit_cast(bf16x8, u);
-}
-
 // Element index of the row (key, kv head g) in the K/V arrays.
 template <bool PAGED>
 __device__ __forceinline__ size_t kv_row(int g, int key, int blk) {
@@ -164,48 +131,75 @@ __device__ __forceinline__ size_t kv_row(int g, int key, int blk) {
   }
 }
 
-__device__ __forceinline__ int clamp_block(const Params& p, int blk) {
-  return min(max(blk, 0), p.num_blocks - 1);
+// ---- LDS tile layout ----
+// A tile holds 64 keys. Each key row (512 B of bf16 K or V, 256 B of int8 K) is cut
+// into 128-byte segments and segment `sg` of all 64 keys is stored contiguously:
+//   byte(key, piece) = (piece >> 3) * kSegStride + key * 128 + (((piece & 7) ^ swz(key)) << 4)
+// with `piece` the 16-byte piece index inside the row and a per-tensor XOR swizzle
+//   K: swz = key & 7         (the 8 lanes of a ds_read_b128 phase read 8 keys at one
+//                             piece and hit 8 different 16-byte bank groups)
+//   V: swz = (key & 3) << 1  (the 4 keys of one 16-lane transposing read land in 4
+//                             different 32-byte bank groups)
+// A global->LDS copy instruction moves 8 keys x one 128-byte segment: every lane
+// group of 8 reads one whole 128-byte line of a key row.
+constexpr int kSegStride = kKt * 128;   // 8 KiB
+
+template <bool V>
+__device__ __forceinline__ int tile_swizzle(int key) {
+  return V ? ((key & 3) << 1) : (key & 7);
 }
 
-// Issue this wave's share of the global -> LDS copies for the KV tile at kbase.
-// Lane t copies key kbase + t (clamped to the last key: keys past kv_len are
-// finite duplicates that the causal mask hides); each instruction moves one
-// 16-byte chunk column of the 64 keys. `blk` is the lane's physical block
-// (paged caches only).
-template <bool PAGED, bool INT8K>
-__device__ __forceinline__ void issue_tile(const Params& p, int g, int kbase, int w, int lane,
-                                           int blk, uint8_t* kbuf, uint8_t* vbuf, float* skbuf) {
-  const int key = min(kbase + lane, p.kv_len - 1);
-  const size_t row = kv_row<PAGED>(g, key, blk);
-  const uint8_t* krow = p.k + row * (INT8K ? 1 : 2);
-  const uint8_t* vrow = p.v + row * 2;
-  constexpr int kKChunks = INT8K ? kD / 16 : kD * 2 / 16;
-  constexpr int kKPerWave = kKChunks / kWaves;
+// Copy this wave's 16 keys (keys 16w .. 16w + 15 of the tile at kbase) of one
+// tensor into an LDS tile. Keys past kv_len are clamped to the last key: finite
+// duplicates that the causal mask hides. `blk` is the wave's physical block (paged).
+template <bool PAGED, bool V, int NSEG>
+__device__ __forceinline__ void copy_rows(const Params& p, const uint8_t* base, int elem_bytes,
+                                          int g, int kbase, int w, int lane, int blk,
+                                          uint8_t* tile) {
+  const int kr = lane >> 3;   // key within an 8-key group
+  const int pp = lane & 7;    // physical piece within the 128-byte segment
 #pragma unroll
-  for (int i = 0; i < kKPerWave; ++i) {
-    const int c = w * kKPerWave + i;
-    __builtin_amdgcn_global_load_lds(krow + c * 16, kbuf + c * kChunkStride, 16, 0, 0);
-  }
+  for (int half = 0; half < 2; ++half) {
+    const int slot = 16 * w + 8 * half + kr;                 // key slot in the tile
+    const int key = min(kbase + slot, p.kv_len - 1);
+    const int piece = pp ^ tile_swizzle<V>(slot);
+    const uint8_t* src = base + kv_row<PAGED>(g, key, blk) * elem_bytes + piece * 16;
+    uint8_t* dst = tile + (16 * w + 8 * half) * 128;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = w * 8 + i;
-    __builtin_amdgcn_global_load_lds(vrow + c * 16, vbuf + c * kChunkStride, 16, 0, 0);
-  }
-  if constexpr (INT8K) {
-    if (w == 0) __builtin_amdgcn_global_load_lds(p.ks + (size_t)key * kHkv + g, skbuf, 4, 0, 0);
+    for (int sg = 0; sg < NSEG; ++sg)
+      __builtin_amdgcn_global_load_lds(src + sg * 128, dst + sg * kSegStride, 16, 0, 0);
   }
 }
 
-// Physical block of the lane's key in the tile at kbase (paged caches).
+// Physical block holding this wave's 16 keys of the tile at kbase (paged caches).
 template <bool PAGED>
-__device__ __forceinline__ int tile_block(const Params& p, int kbase, int lane) {
+__device__ __forceinline__ int wave_block(const Params& p, int kbase, int w) {
   if constexpr (PAGED) {
-    const int key = min(kbase + lane, p.kv_len - 1);
-    return clamp_block(p, p.bt[key >> 4]);
+    const int first = min(kbase + 16 * w, p.kv_len - 1);
+    return min(max(p.bt[first >> 4], 0), p.num_blocks - 1);
   } else {
     return 0;
   }
+}
+
+template <bool PAGED, bool INT8K>
+__device__ __forceinline__ void copy_k(const Params& p, int g, int kbase, int w, int lane,
+                                       uint8_t* ktile, float* sk) {
+  const int blk = wave_block<PAGED>(p, kbase, w);
+  copy_rows<PAGED, false, INT8K ? 2 : 4>(p, p.k, INT8K ? 1 : 2, g, kbase, w, lane, blk, ktile);
+  if constexpr (INT8K) {
+    if (w == 0) {
+      const int key = min(kbase + lane, p.kv_len - 1);
+      __builtin_amdgcn_global_load_lds(p.ks + (size_t)key * kHkv + g, sk, 4, 0, 0);
+    }
+  }
+}
+
+template <bool PAGED>
+__device__ __forceinline__ void copy_v(const Params& p, int g, int kbase, int w, int lane,
+                                       uint8_t* vtile) {
+  const int blk = wave_block<PAGED>(p, kbase, w);
+  copy_rows<PAGED, true, 4>(p, p.v, 2, g, kbase, w, lane, blk, vtile);
 }
 
 __device__ __forceinline__ void wait_vm_all() {
@@ -213,202 +207,174 @@ __device__ __forceinline__ void wait_vm_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// Step N of O^T += V^T · P^T over a 64-key tile: N = 16 ks + db, ks = 32-key half,
-// db = 16-feature block. Issues the transposing reads of step N + 1, waits for
-// step N's, runs its MFMAs.
+// ---- explicit LDS reads ----
+// K fragments are read with inline assembly too, so the prefetch distance is the one
+// written here (the compiler, short of VGPRs, would otherwise serialise each read with
+// its first use). LDS operations of a wave complete in order, so waiting until at most
+// N are outstanding makes every older read's registers valid; the waits tie the
+// registers they guard so no consumer is scheduled above them.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait4(u32x4& a, u32x4& b, u32x4& c, u32x4& d) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
+}
+
+// ---- S^T = K · Q^T for one 64-key tile ----
+// Lane (L, c) reads K fragment (kb, s) = key 16 kb + c, piece 4 s + L:
+//   (s >> 1) * kSegStride + kb * 2048 + c * 128 + (((4 (s & 1) + L) ^ (c & 7)) << 4)
+// i.e. one of two per-lane bases (s even / odd) plus an immediate offset.
+template <bool INT8K, int QB>
+struct QK {
+  using Acc = typename std::conditional<INT8K, i32x4, f32x4>::type;
+  using Frag = typename std::conditional<INT8K, i32x4, bf16x8>::type;
+  static constexpr int kSteps = INT8K ? 4 : 8;
+
+  // The 4 fragments (kb = 0..3) of K step s; `base` = the lane's even- or odd-step base.
+  template <int S>
+  static __device__ __forceinline__ void issue(u32x4 (&f)[4], uint32_t base_even, uint32_t base_odd) {
+    const uint32_t base = (S & 1) ? base_odd : base_even;
+    f[0] = lds_read_b128<(S >> 1) * kSegStride + 0 * 2048>(base);
+    f[1] = lds_read_b128<(S >> 1) * kSegStride + 1 * 2048>(base);
+    f[2] = lds_read_b128<(S >> 1) * kSegStride + 2 * 2048>(base);
+    f[3] = lds_read_b128<(S >> 1) * kSegStride + 3 * 2048>(base);
+  }
+
+  static __device__ __forceinline__ Acc mfma(const u32x4& k, const Frag& q, const Acc& c) {
+    if constexpr (INT8K)
+      return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, k), q, c, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k), q, c, 0, 0, 0);
+  }
+};
+
+// One K step: wait for its fragments (the next step's 4 reads may stay in flight),
+// issue the reads of step S + 1, run the 4 x QB MFMAs of step S, then `extra(S)`.
+template <bool INT8K, int QB, int S, class Extra>
+__device__ __forceinline__ void qk_steps(u32x4 (&kf)[2][4], uint32_t be, uint32_t bo,
+                                         const typename QK<INT8K, QB>::Frag (&qf)[QB][QK<INT8K, QB>::kSteps],
+                                         typename QK<INT8K, QB>::Acc (&acc)[QB][4], Extra&& extra) {
+  using Q = QK<INT8K, QB>;
+  if constexpr (S + 1 < Q::kSteps) {
+    Q::template issue<S + 1>(kf[(S + 1) & 1], be, bo);
+    lds_wait4<4>(kf[S & 1][0], kf[S & 1][1], kf[S & 1][2], kf[S & 1][3]);
+  } else {
+    lds_wait4<0>(kf[S & 1][0], kf[S & 1][1], kf[S & 1][2], kf[S & 1][3]);
+  }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int b = 0; b < QB; ++b) acc[b][kb] = Q::mfma(kf[S & 1][kb], qf[b][S], acc[b][kb]);
+  extra(S);
+  if constexpr (S + 1 < Q::kSteps) qk_steps<INT8K, QB, S + 1>(kf, be, bo, qf, acc, extra);
+}
+
+// ---- O^T += V^T · P^T (and l += 1 · P^T) ----
+// Transposing read: lane i of 16-lane group L fetches features 16 db + 4 (i & 3) .. +3 of
+// key 32 ks + 16 h + 4 L + (i >> 2); after the transpose lane (L, c) holds
+// V[32 ks + 16 h + 4 L + k][16 db + c], k = 0..3, exactly its P^T operand's keys.
+struct VtFrag {
+  uint2 lo, hi;
+};
+
+// Issued as inline assembly so the compiler does not make these reads wait for the
+// global->LDS copies into other buffers; vt_wait must run before the registers are used.
+template <int OFF>
+__device__ __forceinline__ void vt_issue(VtFrag& f, uint32_t addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%3\n\tds_read_b64_tr_b16 %1, %2 offset:%4"
+               : "=v"(f.lo), "=v"(f.hi)
+               : "v"(addr), "i"(OFF), "i"(OFF + 16 * 128));
+}
+
+// Wait until at most N LDS operations of this wave are outstanding (LDS operations
+// complete in order), tying the fragment's registers to the wait.
+template <int N>
+__device__ __forceinline__ void vt_wait(VtFrag& f) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(f.lo), "+v"(f.hi) : "i"(N));
+}
+
+__device__ __forceinline__ bf16x8 vt_value(const VtFrag& f) {
+  return __builtin_bit_cast(bf16x8, make_uint4(f.lo.x, f.lo.y, f.hi.x, f.hi.y));
+}
+
+// Step N = 16 ks + db: ks = 32-key half of the tile, db = 16-feature block.
+// V^T fragment (ks, db) sits at vbase[db & 3] + (db >> 2) * kSegStride + ks * 4096.
+// Fragments travel in a ring of kVtDepth + 1: step N issues the reads of step
+// N + kVtDepth, then waits for its own (2 reads per step).
+constexpr int kVtDepth = 3;
+
+template <int N>
+__device__ __forceinline__ void vt_issue_step(VtFrag& f, const uint32_t (&vbase)[4]) {
+  constexpr int ks = N >> 4, db = N & 15;
+  vt_issue<(db >> 2) * kSegStride + ks * 4096>(f, vbase[db & 3]);
+}
+
 template <int N, int QB, bool SPLIT>
 struct PvStep {
-  static __device__ __forceinline__ void run(VtFrag (&vf)[2], uint32_t vaddr,
+  static __device__ __forceinline__ void run(VtFrag (&vf)[kVtDepth + 1], const uint32_t (&vbase)[4],
                                              const bf16x8 (&ph)[QB][2], const bf16x8 (&pl)[QB][2],
-                                             f32x4 (&o)[16][QB]) {
+                                             const bf16x8& ones, f32x4 (&o)[16][QB],
+                                             f32x4 (&lacc)[QB]) {
     constexpr int ks = N >> 4, db = N & 15;
-    if constexpr (N + 1 < 32) {
-      constexpr int ks1 = (N + 1) >> 4, db1 = (N + 1) & 15;
-      vt_issue<db1 * 2 * kChunkStride + 32 * ks1 * 16>(vf[(N + 1) & 1], vaddr);
-      vt_wait<2>(vf[N & 1]);
-    } else {
-      vt_wait<0>(vf[N & 1]);
-    }
-    const bf16x8 v = vt_value(vf[N & 1]);
+    constexpr int kAhead = (32 - 1 - N) < kVtDepth ? (32 - 1 - N) : kVtDepth;  // steps in flight after N
+    if constexpr (N + kVtDepth < 32) vt_issue_step<N + kVtDepth>(vf[(N + kVtDepth) % (kVtDepth + 1)], vbase);
+    vt_wait<2 * kAhead>(vf[N % (kVtDepth + 1)]);
+    const bf16x8 v = vt_value(vf[N % (kVtDepth + 1)]);
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
       o[db][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, ph[b][ks], o[db][b], 0, 0, 0);
       if constexpr (SPLIT)
         o[db][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pl[b][ks], o[db][b], 0, 0, 0);
     }
-    if constexpr (N + 1 < 32) PvStep<N + 1, QB, SPLIT>::run(vf, vaddr, ph, pl, o);
-  }
-};
-
-template <bool PAGED, bool INT8K, int QB>
-struct Tile {
-  // S^T for 64 keys x (QB x 16) columns, P and the running softmax state
-  template <bool SPLIT>
-  static __device__ __forceinline__ void compute(const uint8_t* kbuf, const uint8_t* vbuf,
-                                                 const float* skbuf, int kbase, int L, int c,
-                                                 int lane, bool diag, int limit,
-                                                 const bf16x8 (&qf)[INT8K ? 1 : QB][INT8K ? 1 : 8],
-                                                 const i32x4 (&qq)[INT8K ? QB : 1][INT8K ? 4 : 1],
-                                                 const float (&qs)[QB], float (&m)[QB],
-                                                 float (&l)[QB], f32x4 (&o)[16][QB]) {
-    // ---- S^T = K · Q^T ----
-    float sc[QB][16];   // [query block][key slot 4 kb + r] for key 16 kb + 4 L + r
-    const int koff = L * kChunkStride + c * 16;
-    if constexpr (!INT8K) {
-      f32x4 acc[QB][4];
-#pragma unroll
-      for (int b = 0; b < QB; ++b)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc[b][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // K fragments for step s + 1 are read while the MFMAs of step s run
-      bf16x8 kf[2][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        kf[0][kb] = *reinterpret_cast<const bf16x8*>(kbuf + koff + kb * 256);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        if (s + 1 < 8) {
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-            kf[(s + 1) & 1][kb] = *reinterpret_cast<const bf16x8*>(
-                kbuf + koff + 4 * (s + 1) * kChunkStride + kb * 256);
-        }
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int b = 0; b < QB; ++b)
-            acc[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s & 1][kb], qf[b][s], acc[b][kb],
-                                                                 0, 0, 0);
-      }
-#pragma unroll
-      for (int b = 0; b < QB; ++b)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[b][4 * kb + r] = acc[b][kb][r] * kLog2eOver16;
-    } else {
-      i32x4 acc[QB][4];
-#pragma unroll
-      for (int b = 0; b < QB; ++b)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc[b][kb] = i32x4{0, 0, 0, 0};
-      i32x4 kf[2][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        kf[0][kb] = *reinterpret_cast<const i32x4*>(kbuf + koff + kb * 256);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (s + 1 < 4) {
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-            kf[(s + 1) & 1][kb] = *reinterpret_cast<const i32x4*>(
-                kbuf + koff + 4 * (s + 1) * kChunkStride + kb * 256);
-        }
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int b = 0; b < QB; ++b)
-            acc[b][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf[s & 1][kb], qq[b][s], acc[b][kb],
-                                                               0, 0, 0);
-      }
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const f32x4 sk = *reinterpret_cast<const f32x4*>(skbuf + 16 * kb + 4 * L);
-#pragma unroll
-        for (int b = 0; b < QB; ++b)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[b][4 * kb + r] = (float)acc[b][kb][r] * sk[r] * qs[b];
-      }
-    }
-
-    // ---- causal mask (only tiles that reach past the workgroup's first query) ----
-    if (diag) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kbase + 16 * kb + 4 * L + r;
-          if (key > limit) {
-#pragma unroll
-            for (int b = 0; b < QB; ++b) sc[b][4 * kb + r] = -__builtin_inff();
-          }
-        }
-    }
-
-    // ---- online softmax (exp2 domain, lazy rescale) ----
-    float mnew[QB];
-    bool need = false;
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      float mx = sc[b][0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[b][e]);
-      mx = xor16_max(mx);
-      mx = xor32_max(mx);
-      mnew[b] = fmaxf(m[b], mx);
-      need = need || (mnew[b] > m[b] + kTau);
-    }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    if constexpr (db == 0) {
+      // row sums from the same bf16 P the P·V product uses
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
-        const float alpha = __builtin_amdgcn_exp2f(m[b] - mnew[b]);
-        m[b] = mnew[b];
-        l[b] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 16; ++db) o[db][b] *= alpha;
+        lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ph[b][ks], lacc[b], 0, 0, 0);
+        if constexpr (SPLIT)
+          lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl[b][ks], lacc[b], 0, 0, 0);
       }
     }
-    // P^T operands: k-step ks covers keys 32 ks .. 32 ks + 31; a lane's 8 elements are
-    // keys 32 ks + 4 L + {0..3} and 32 ks + 16 + 4 L + {0..3} = its S^T slots 8 ks .. 8 ks + 7
-    bf16x8 ph[QB][2], pl[QB][2];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      float sum = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        f32x8 pv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(sc[b][8 * ks + e] - m[b]);
-        ph[b][ks] = __builtin_convertvector(pv, bf16x8);
-        const f32x8 hi = __builtin_convertvector(ph[b][ks], f32x8);
-        if constexpr (SPLIT) {
-          pl[b][ks] = __builtin_convertvector(pv - hi, bf16x8);
-          const f32x8 lo = __builtin_convertvector(pl[b][ks], f32x8);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sum += hi[e] + lo[e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sum += hi[e];
-        }
-      }
-      l[b] += sum;
-    }
-
-    // ---- O^T += V^T · P^T ----
-    // transposing read: lane i of 16-lane group L fetches features 16 db + 4 (i & 3) .. +3 of
-    // key 32 ks + 16 h + 4 L + (i >> 2); after the transpose lane (L, c) holds
-    // V[32 ks + 16 h + 4 L + k][16 db + c] for k = 0..3
-    const int voff = ((c & 3) >> 1) * kChunkStride + (4 * L + (c >> 2)) * 16 + 8 * (c & 1);
-    // V^T fragments for step n + 1 (n = 16 ks + db) are read while the MFMAs of step n run
-    VtFrag vf[2];
-    const uint32_t vaddr = lds_addr(vbuf) + voff;
-    vt_issue<0>(vf[0], vaddr);
-    PvStep<0, QB, SPLIT>::run(vf, vaddr, ph, pl, o);
+    if constexpr (N + 1 < 32) PvStep<N + 1, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc);
   }
 };
 
 template <bool PAGED, bool INT8K, int QB>
-constexpr int stage_bytes() {
-  return (INT8K ? kKTileI8 : kKTileBf16) + kVTile + (INT8K ? kSkTile : 0);
+constexpr int k_tile_bytes() {
+  return (INT8K ? 2 : 4) * kSegStride;
+}
+
+// LDS: two K tiles, two V tiles and (INT8 keys) a 3-slot ring of key-scale rows.
+template <bool PAGED, bool INT8K, int QB>
+constexpr int lds_bytes() {
+  return 2 * k_tile_bytes<PAGED, INT8K, QB>() + 2 * 4 * kSegStride + (INT8K ? 3 * kSkTile : 0);
 }
 
 // The whole workgroup program. SPLIT selects the P·V form (see the file header); it
 // is fixed per workgroup, so each form is a separate straight-line program.
+//
+// Software pipeline over KV tiles: iteration j holds S(j) from the previous
+// iteration, computes P(j) while the MFMAs of S(j+1) = K(j+1)·Q^T run, then
+// O += V(j)·P(j). LDS holds K(j+1) and V(j) while K(j+2) and V(j+1) are copied in.
 template <bool PAGED, bool INT8K, int QB, bool SPLIT>
 __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   using S = Shape<QB>;
-  constexpr int kKTile = INT8K ? kKTileI8 : kKTileBf16;
-  constexpr int kStage = stage_bytes<PAGED, INT8K, QB>();
+  using Q = QK<INT8K, QB>;
+  using Acc = typename Q::Acc;
+  constexpr int kKTile = k_tile_bytes<PAGED, INT8K, QB>();
+  constexpr int kVOff = 2 * kKTile;                    // V tiles follow the two K tiles
+  constexpr int kSkOff = kVOff + 8 * kSegStride;       // then the key-scale ring
+  // (buffers are addressed as smem + offset so every access stays an LDS access)
+  float* const skring = reinterpret_cast<float*>(smem + kSkOff);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -438,16 +404,14 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   const int last_tok = min(t0 + S::kTokPerWg, p.q_len);
   const int ntiles = (off + last_tok + kKt - 1) / kKt;
 
-  // start the first tile's copies before the Q prologue
-  int blk = tile_block<PAGED>(p, 0, lane);
-  issue_tile<PAGED, INT8K>(p, g, 0, w, lane, blk, smem, smem + kKTile,
-                           reinterpret_cast<float*>(smem + kKTile + kVTile));
-  if (ntiles > 1) blk = tile_block<PAGED>(p, kKt, lane);
+  // start the first copies before the Q prologue
+  copy_k<PAGED, INT8K>(p, g, 0, w, lane, smem, skring);
+  copy_v<PAGED>(p, g, 0, w, lane, smem + kVOff);
+  if (ntiles > 1) copy_k<PAGED, INT8K>(p, g, kKt, w, lane, smem + kKTile, skring + kKt);
 
   // ---- prologue: Q fragments (B operand of S^T = K·Q^T) ----
-  bf16x8 qf[INT8K ? 1 : QB][INT8K ? 1 : 8];
-  i32x4 qq[INT8K ? QB : 1][INT8K ? 4 : 1];
-  float qs[QB];
+  typename Q::Frag qf[QB][Q::kSteps];
+  float qs[QB];   // log2(e)/16, times sQ with INT8 keys
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const uint8_t* qrow = p.q + ((size_t)tok * kHq + head0 + b) * kD * 2;
@@ -496,48 +460,173 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
           }
           wv[j] = packed;
         }
-        qq[b][s] = i32x4{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
+        qf[b][s] = i32x4{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
       }
     }
   }
 
-  // ---- accumulators: O^T blocks [feature block db][query block b] ----
+  // ---- per-lane LDS bases ----
+  const int kb_even = c * 128 + ((L ^ (c & 7)) << 4);
+  const int kb_odd = c * 128 + (((L ^ (c & 7)) ^ 4) << 4);
+  uint32_t vbase_off[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+    vbase_off[jj] = (4 * L + (c >> 2)) * 128 + ((2 * (jj ^ (c >> 2)) + ((c & 3) >> 1)) << 4) +
+                    8 * (c & 1);
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+
+  // ---- accumulators: O^T blocks [feature block db][query block b], row sums ----
   f32x4 o[16][QB];
-#pragma unroll
-  for (int db = 0; db < 16; ++db)
-#pragma unroll
-    for (int b = 0; b < QB; ++b) o[db][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[QB], l[QB];
+  f32x4 lacc[QB];
+  float m[QB];
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
+#pragma unroll
+    for (int db = 0; db < 16; ++db) o[db][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    lacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[b] = -__builtin_inff();
-    l[b] = 0.0f;
   }
 
-  using T = Tile<PAGED, INT8K, QB>;
+  // ---- S(0) ----
+  Acc sacc[QB][4];
+  const uint32_t smem_addr = lds_addr(smem);
+  wait_vm_all();
+  __syncthreads();
+  {
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) sacc[b][kb] = Acc{0, 0, 0, 0};
+    u32x4 kf[2][4];
+    Q::template issue<0>(kf[0], smem_addr + kb_even, smem_addr + kb_odd);
+    qk_steps<INT8K, QB, 0>(kf, smem_addr + kb_even, smem_addr + kb_odd, qf, sacc, [](int) {});
+  }
+  __syncthreads();   // every wave is done with K(0) before K(2) overwrites it
+
   for (int j = 0; j < ntiles; ++j) {
     const int kbase = j * kKt;
-    uint8_t* cur = smem + (j & 1) * kStage;
-    uint8_t* nxt = smem + ((j + 1) & 1) * kStage;
-    wait_vm_all();
-    __syncthreads();   // tile j is in `cur`; everyone is done with `nxt` (tile j - 1)
-    if (j + 1 < ntiles) {
-      issue_tile<PAGED, INT8K>(p, g, kbase + kKt, w, lane, blk, nxt, nxt + kKTile,
-                               reinterpret_cast<float*>(nxt + kKTile + kVTile));
-      if (j + 2 < ntiles) blk = tile_block<PAGED>(p, kbase + 2 * kKt, lane);
+    const uint8_t* knext = smem + ((j + 1) & 1) * kKTile;             // K(j+1) (stale on the last tile)
+    const uint8_t* vcur = smem + kVOff + (j & 1) * 4 * kSegStride;   // V(j)
+    if (j + 2 < ntiles)
+      copy_k<PAGED, INT8K>(p, g, kbase + 2 * kKt, w, lane, smem + (j & 1) * kKTile,
+                           skring + ((j + 2) % 3) * kKt);
+    if (j + 1 < ntiles)
+      copy_v<PAGED>(p, g, kbase + kKt, w, lane, smem + kVOff + ((j + 1) & 1) * 4 * kSegStride);
+
+    // ---- scores of tile j in log2 units (bf16: raw, scaled inside the exponent) ----
+    float sc[QB][16];
+    float scale[QB];
+    if constexpr (!INT8K) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        scale[b] = kLog2eOver16;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[b][4 * kb + r] = sacc[b][kb][r];
+      }
+    } else {
+      const float* sk = skring + (j % 3) * kKt;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const f32x4 skv = *reinterpret_cast<const f32x4*>(sk + 16 * kb + 4 * L);
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[b][4 * kb + r] = (float)sacc[b][kb][r] * (skv[r] * qs[b]);
+      }
+#pragma unroll
+      for (int b = 0; b < QB; ++b) scale[b] = 1.0f;
     }
-    T::template compute<SPLIT>(cur, cur + kKTile, reinterpret_cast<const float*>(cur + kKTile + kVTile),
-                               kbase, L, c, lane, kbase + kKt - 1 > off + t0, limit, qf, qq, qs, m,
-                               l, o);
+    // causal mask (only tiles that reach past the workgroup's first query)
+    if (kbase + kKt - 1 > off + t0) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kbase + 16 * kb + 4 * L + r;
+          if (key > limit) {
+#pragma unroll
+            for (int b = 0; b < QB; ++b) sc[b][4 * kb + r] = -__builtin_inff();
+          }
+        }
+    }
+    // ---- online softmax: column maxima, lazy rescale ----
+    float mnew[QB];
+    bool need = false;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      float mx = sc[b][0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[b][e]);
+      mx = xor16_max(mx);
+      mx = xor32_max(mx);
+      mnew[b] = fmaxf(m[b], mx * scale[b]);
+      need = need || (mnew[b] > m[b] + kTau);
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        const float alpha = __builtin_amdgcn_exp2f(m[b] - mnew[b]);
+        m[b] = mnew[b];
+        lacc[b] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 16; ++db) o[db][b] *= alpha;
+      }
+    }
+
+    // ---- P(j), interleaved with S(j+1) = K(j+1) · Q^T ----
+    bf16x8 ph[QB][2], pl[QB][2];
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) sacc[b][kb] = Acc{0, 0, 0, 0};
+    {
+      const uint32_t kn = lds_addr(knext);
+      u32x4 kf[2][4];
+      Q::template issue<0>(kf[0], kn + kb_even, kn + kb_odd);
+      // one (query block, key half) of P per two K steps (per K step with INT8 keys)
+      constexpr int kPer = Q::kSteps / (2 * QB) > 0 ? Q::kSteps / (2 * QB) : 1;
+      auto softmax_part = [&](int st) {
+        if ((st + 1) % kPer == 0 && (st + 1) / kPer <= 2 * QB) {
+          const int idx = (st + 1) / kPer - 1;
+          const int b = idx >> 1, ks = idx & 1;
+          const float nm = -m[b];
+          f32x8 pv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][8 * ks + e], scale[b], nm));
+          ph[b][ks] = __builtin_convertvector(pv, bf16x8);
+          if constexpr (SPLIT)
+            pl[b][ks] = __builtin_convertvector(pv - __builtin_convertvector(ph[b][ks], f32x8), bf16x8);
+        }
+      };
+      qk_steps<INT8K, QB, 0>(kf, kn + kb_even, kn + kb_odd, qf, sacc, softmax_part);
+    }
+
+    // ---- O^T += V^T(j) · P^T(j) ----
+    {
+      uint32_t vbase[4];
+      const uint32_t v0 = lds_addr(vcur);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) vbase[jj] = v0 + vbase_off[jj];
+      VtFrag vf[kVtDepth + 1];
+      vt_issue_step<0>(vf[0], vbase);
+      vt_issue_step<1>(vf[1], vbase);
+      vt_issue_step<2>(vf[2], vbase);
+      PvStep<0, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc);
+    }
+
+    wait_vm_all();
+    __syncthreads();   // K(j+2), V(j+1) landed; everyone is done with K(j+1) and V(j)
   }
 
   // ---- epilogue: O / l -> bf16 ----
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
-    float lt = l[b];
-    lt = xor16_sum(lt);
-    lt = xor32_sum(lt);
-    const float inv = 1.0f / lt;
+    const float inv = 1.0f / lacc[b][0];
     if (tok_ok) {
       uint8_t* orow = p.out + ((size_t)tok * kHq + head0 + b) * kD * 2;
 #pragma unroll
@@ -553,7 +642,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
 template <bool PAGED, bool INT8K, int QB>
 __global__ __launch_bounds__(kThreads, 1) void gqa_prefill_kernel(const Params p) {
   using S = Shape<QB>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * stage_bytes<PAGED, INT8K, QB>()];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[lds_bytes<PAGED, INT8K, QB>()];
   const int rest = blockIdx.x >> 2;
   const int t0 = (p.n_tblk - 1 - rest / S::kSplitsPerGroup) * S::kTokPerWg;
   if (p.kv_len - p.q_len + t0 + 1 < kSplitBelow)
@@ -620,7 +709,7 @@ Launch shape_launch(int32_t q_len, bool int8k) {
   lc.n_tblk = n_tblk;
   lc.workgroups = n_tblk * kHkv * S::kSplitsPerGroup;
   lc.threads = kThreads;
-  lc.lds_bytes = 2 * ((int8k ? kKTileI8 : kKTileBf16) + kVTile + (int8k ? kSkTile : 0));
+  lc.lds_bytes = int8k ? lds_bytes<false, true, QB>() : lds_bytes<false, false, QB>();
   return lc;
 }
 
