@@ -63,7 +63,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKt = 64;                  // keys per KV tile
 constexpr int kSplitBelow = 256;
-constexpr float kTau = 8.0f;
+constexpr float kTau = 32.0f;   // log2 headroom of the reference maximum
 constexpr float kLog2eOver16 = 1.4426950408889634f / 16.0f;
 
 constexpr int kSkTile = kKt * 4;         // 256 B of key scales per tile
@@ -151,42 +151,46 @@ __device__ __forceinline__ int tile_swizzle(int key) {
 
 // Copy this wave's 16 keys (keys 16w .. 16w + 15 of the tile at kbase) of one
 // tensor into an LDS tile. Keys past kv_len are clamped to the last key: finite
-// duplicates that the causal mask hides. `blk` is the wave's physical block (paged).
+// duplicates that the causal mask hides. The wave's 16 keys lie in one 16-key block,
+// so the source is a wave-uniform base (the wave's first row, or its physical block)
+// plus a small per-lane offset. `w` is wave-uniform.
 template <bool PAGED, bool V, int NSEG>
 __device__ __forceinline__ void copy_rows(const Params& p, const uint8_t* base, int elem_bytes,
-                                          int g, int kbase, int w, int lane, int blk,
-                                          uint8_t* tile) {
+                                          int g, int kbase, int w, int lane, uint8_t* tile) {
   const int kr = lane >> 3;   // key within an 8-key group
   const int pp = lane & 7;    // physical piece within the 128-byte segment
+  const int row_bytes = kD * elem_bytes;
+  const int first = min(kbase + 16 * w, p.kv_len - 1);   // wave-uniform
+  const uint8_t* wbase;
+  if constexpr (PAGED) {
+    const int blk = min(max(p.bt[first >> 4], 0), p.num_blocks - 1);
+    wbase = base + ((size_t)(blk * kHkv + g) * kBs) * row_bytes;
+  } else {
+    wbase = base + ((size_t)first * kHkv + g) * row_bytes;
+  }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    const int slot = 16 * w + 8 * half + kr;                 // key slot in the tile
+    const int slot = 16 * w + 8 * half + kr;            // key slot in the tile
     const int key = min(kbase + slot, p.kv_len - 1);
     const int piece = pp ^ tile_swizzle<V>(slot);
-    const uint8_t* src = base + kv_row<PAGED>(g, key, blk) * elem_bytes + piece * 16;
+    uint32_t voff;
+    if constexpr (PAGED)
+      voff = (uint32_t)((key & (kBs - 1)) * row_bytes + piece * 16);
+    else
+      voff = (uint32_t)((key - first) * (kHkv * row_bytes) + piece * 16);
     uint8_t* dst = tile + (16 * w + 8 * half) * 128;
 #pragma unroll
-    for (int sg = 0; sg < NSEG; ++sg)
-      __builtin_amdgcn_global_load_lds(src + sg * 128, dst + sg * kSegStride, 16, 0, 0);
-  }
-}
-
-// Physical block holding this wave's 16 keys of the tile at kbase (paged caches).
-template <bool PAGED>
-__device__ __forceinline__ int wave_block(const Params& p, int kbase, int w) {
-  if constexpr (PAGED) {
-    const int first = min(kbase + 16 * w, p.kv_len - 1);
-    return min(max(p.bt[first >> 4], 0), p.num_blocks - 1);
-  } else {
-    return 0;
+    for (int sg = 0; sg < NSEG; ++sg) {
+      const uint8_t* sbase = wbase + sg * 128;   // uniform: the segment step stays scalar
+      __builtin_amdgcn_global_load_lds(sbase + voff, dst + sg * kSegStride, 16, 0, 0);
+    }
   }
 }
 
 template <bool PAGED, bool INT8K>
 __device__ __forceinline__ void copy_k(const Params& p, int g, int kbase, int w, int lane,
                                        uint8_t* ktile, float* sk) {
-  const int blk = wave_block<PAGED>(p, kbase, w);
-  copy_rows<PAGED, false, INT8K ? 2 : 4>(p, p.k, INT8K ? 1 : 2, g, kbase, w, lane, blk, ktile);
+  copy_rows<PAGED, false, INT8K ? 2 : 4>(p, p.k, INT8K ? 1 : 2, g, kbase, w, lane, ktile);
   if constexpr (INT8K) {
     if (w == 0) {
       const int key = min(kbase + lane, p.kv_len - 1);
@@ -198,8 +202,7 @@ __device__ __forceinline__ void copy_k(const Params& p, int g, int kbase, int w,
 template <bool PAGED>
 __device__ __forceinline__ void copy_v(const Params& p, int g, int kbase, int w, int lane,
                                        uint8_t* vtile) {
-  const int blk = wave_block<PAGED>(p, kbase, w);
-  copy_rows<PAGED, true, 4>(p, p.v, 2, g, kbase, w, lane, blk, vtile);
+  copy_rows<PAGED, true, 4>(p, p.v, 2, g, kbase, w, lane, vtile);
 }
 
 __device__ __forceinline__ void wait_vm_all() {
@@ -353,10 +356,11 @@ constexpr int k_tile_bytes() {
   return (INT8K ? 2 : 4) * kSegStride;
 }
 
-// LDS: two K tiles, two V tiles and (INT8 keys) a 3-slot ring of key-scale rows.
+// LDS: two K tiles, two V tiles, (INT8 keys) a 3-slot ring of key-scale rows, and
+// two slots of one restart flag per wave.
 template <bool PAGED, bool INT8K, int QB>
 constexpr int lds_bytes() {
-  return 2 * k_tile_bytes<PAGED, INT8K, QB>() + 2 * 4 * kSegStride + (INT8K ? 3 * kSkTile : 0);
+  return 2 * k_tile_bytes<PAGED, INT8K, QB>() + 2 * 4 * kSegStride + (INT8K ? 3 * kSkTile : 0) + 32;
 }
 
 // The whole workgroup program. SPLIT selects the P·V form (see the file header); it
@@ -373,12 +377,13 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   constexpr int kKTile = k_tile_bytes<PAGED, INT8K, QB>();
   constexpr int kVOff = 2 * kKTile;                    // V tiles follow the two K tiles
   constexpr int kSkOff = kVOff + 8 * kSegStride;       // then the key-scale ring
+  constexpr int kFlagOff = kSkOff + (INT8K ? 3 * kSkTile : 0);   // then the restart flags
   // (buffers are addressed as smem + offset so every access stays an LDS access)
   float* const skring = reinterpret_cast<float*>(smem + kSkOff);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int L = lane >> 4;      // k-group of the MFMA operands / row group of the output
   const int c = lane & 15;      // query column (token) inside a 16-column block
   const int tw = w % S::kTokenBlocks;
@@ -480,44 +485,24 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   // ---- accumulators: O^T blocks [feature block db][query block b], row sums ----
   f32x4 o[16][QB];
   f32x4 lacc[QB];
-  float m[QB];
-#pragma unroll
-  for (int b = 0; b < QB; ++b) {
-#pragma unroll
-    for (int db = 0; db < 16; ++db) o[db][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    lacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[b] = -__builtin_inff();
-  }
-
-  // ---- S(0) ----
+  float m[QB];   // reference maximum per column (log2 units), fixed during a pass
   Acc sacc[QB][4];
   const uint32_t smem_addr = lds_addr(smem);
-  wait_vm_all();
-  __syncthreads();
-  {
+  int* const flags = reinterpret_cast<int*>(smem + kFlagOff);
+
+  // S^T of the tile in K buffer `kbuf` into sacc
+  auto qk_tile = [&](uint32_t kbuf) {
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) sacc[b][kb] = Acc{0, 0, 0, 0};
     u32x4 kf[2][4];
-    Q::template issue<0>(kf[0], smem_addr + kb_even, smem_addr + kb_odd);
-    qk_steps<INT8K, QB, 0>(kf, smem_addr + kb_even, smem_addr + kb_odd, qf, sacc, [](int) {});
-  }
-  __syncthreads();   // every wave is done with K(0) before K(2) overwrites it
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int kbase = j * kKt;
-    const uint8_t* knext = smem + ((j + 1) & 1) * kKTile;             // K(j+1) (stale on the last tile)
-    const uint8_t* vcur = smem + kVOff + (j & 1) * 4 * kSegStride;   // V(j)
-    if (j + 2 < ntiles)
-      copy_k<PAGED, INT8K>(p, g, kbase + 2 * kKt, w, lane, smem + (j & 1) * kKTile,
-                           skring + ((j + 2) % 3) * kKt);
-    if (j + 1 < ntiles)
-      copy_v<PAGED>(p, g, kbase + kKt, w, lane, smem + kVOff + ((j + 1) & 1) * 4 * kSegStride);
-
-    // ---- scores of tile j in log2 units (bf16: raw, scaled inside the exponent) ----
-    float sc[QB][16];
-    float scale[QB];
+    Q::template issue<0>(kf[0], kbuf + kb_even, kbuf + kb_odd);
+    qk_steps<INT8K, QB, 0>(kf, kbuf + kb_even, kbuf + kb_odd, qf, sacc, [](int) {});
+  };
+  // scores of the tile at kbase from sacc, in log2 units once multiplied by scale[b]
+  // (bf16: raw dot products; INT8 keys: already scaled), causal mask applied
+  auto tile_scores = [&](const float* sk, int kbase, float (&sc)[QB][16], float (&scale)[QB]) {
     if constexpr (!INT8K) {
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
@@ -528,7 +513,6 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
           for (int r = 0; r < 4; ++r) sc[b][4 * kb + r] = sacc[b][kb][r];
       }
     } else {
-      const float* sk = skring + (j % 3) * kKt;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const f32x4 skv = *reinterpret_cast<const f32x4*>(sk + 16 * kb + 4 * L);
@@ -540,8 +524,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
 #pragma unroll
       for (int b = 0; b < QB; ++b) scale[b] = 1.0f;
     }
-    // causal mask (only tiles that reach past the workgroup's first query)
-    if (kbase + kKt - 1 > off + t0) {
+    if (kbase + kKt - 1 > off + t0) {   // only tiles that reach past the workgroup's first query
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -553,74 +536,141 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
           }
         }
     }
-    // ---- online softmax: column maxima, lazy rescale ----
-    float mnew[QB];
-    bool need = false;
+  };
+  // this lane's maximum of each column (not yet reduced over the 4 lanes of a column)
+  auto lane_max = [&](const float (&sc)[QB][16], int b) {
+    float mx = sc[b][0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[b][e]);
+    return mx;
+  };
+
+  // Pass 0 takes each column's maximum over tile 0 as the reference and checks every
+  // later tile against it: a score more than 2^kTau above the reference makes the
+  // whole workgroup start again (pass 1) with the exact column maxima over all its
+  // keys, found by a max-only sweep. Either way no accumulator is ever rescaled.
+  for (int pass = 0;; ++pass) {
+    if (pass > 0) {
+      copy_k<PAGED, INT8K>(p, g, 0, w, lane, smem, skring);
+      copy_v<PAGED>(p, g, 0, w, lane, smem + kVOff);
+      if (ntiles > 1) copy_k<PAGED, INT8K>(p, g, kKt, w, lane, smem + kKTile, skring + kKt);
+    }
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
-      float mx = sc[b][0];
 #pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[b][e]);
-      mx = xor16_max(mx);
-      mx = xor32_max(mx);
-      mnew[b] = fmaxf(m[b], mx * scale[b]);
-      need = need || (mnew[b] > m[b] + kTau);
+      for (int db = 0; db < 16; ++db) o[db][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      lacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    if (pass == 0 && tid < 8) flags[tid] = 0;
+    wait_vm_all();
+    __syncthreads();
+    qk_tile(smem_addr);   // S(0)
+    if (pass == 0) {
+      float sc[QB][16], scale[QB];
+      tile_scores(skring, 0, sc, scale);
 #pragma unroll
-      for (int b = 0; b < QB; ++b) {
-        const float alpha = __builtin_amdgcn_exp2f(m[b] - mnew[b]);
-        m[b] = mnew[b];
-        lacc[b] *= alpha;
+      for (int b = 0; b < QB; ++b) m[b] = xor32_max(xor16_max(lane_max(sc, b))) * scale[b];
+    }
+    __syncthreads();   // every wave is done with K(0) before K(2) overwrites it
+
+    bool restart = false;
+    int flag_seen = 0;   // flags read after the previous tile's barrier
+    for (int j = 0; j < ntiles; ++j) {
+      const int kbase = j * kKt;
+      const uint8_t* knext = smem + ((j + 1) & 1) * kKTile;             // K(j+1) (stale on the last tile)
+      const uint8_t* vcur = smem + kVOff + (j & 1) * 4 * kSegStride;   // V(j)
+      if (j + 2 < ntiles)
+        copy_k<PAGED, INT8K>(p, g, kbase + 2 * kKt, w, lane, smem + (j & 1) * kKTile,
+                             skring + ((j + 2) % 3) * kKt);
+      if (j + 1 < ntiles)
+        copy_v<PAGED>(p, g, kbase + kKt, w, lane, smem + kVOff + ((j + 1) & 1) * 4 * kSegStride);
+
+      float sc[QB][16], scale[QB];
+      tile_scores(skring + (j % 3) * kKt, kbase, sc, scale);
+      bool over = false;
+      if (pass == 0) {
 #pragma unroll
-        for (int db = 0; db < 16; ++db) o[db][b] *= alpha;
+        for (int b = 0; b < QB; ++b) over = over || (lane_max(sc, b) * scale[b] > m[b] + kTau);
+      }
+
+      // ---- P(j), interleaved with S(j+1) = K(j+1) · Q^T ----
+      bf16x8 ph[QB][2], pl[QB][2];
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) sacc[b][kb] = Acc{0, 0, 0, 0};
+      {
+        const uint32_t kn = lds_addr(knext);
+        u32x4 kf[2][4];
+        Q::template issue<0>(kf[0], kn + kb_even, kn + kb_odd);
+        // one (query block, key half) of P per two K steps (per K step with INT8 keys)
+        constexpr int kPer = Q::kSteps / (2 * QB) > 0 ? Q::kSteps / (2 * QB) : 1;
+        auto softmax_part = [&](int st) {
+          if ((st + 1) % kPer == 0 && (st + 1) / kPer <= 2 * QB) {
+            const int idx = (st + 1) / kPer - 1;
+            const int b = idx >> 1, ks = idx & 1;
+            const float nm = -m[b];
+            f32x8 pv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][8 * ks + e], scale[b], nm));
+            ph[b][ks] = __builtin_convertvector(pv, bf16x8);
+            if constexpr (SPLIT)
+              pl[b][ks] = __builtin_convertvector(pv - __builtin_convertvector(ph[b][ks], f32x8), bf16x8);
+          }
+        };
+        qk_steps<INT8K, QB, 0>(kf, kn + kb_even, kn + kb_odd, qf, sacc, softmax_part);
+      }
+
+      // ---- O^T += V^T(j) · P^T(j) ----
+      {
+        uint32_t vbase[4];
+        const uint32_t v0 = lds_addr(vcur);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) vbase[jj] = v0 + vbase_off[jj];
+        VtFrag vf[kVtDepth + 1];
+        vt_issue_step<0>(vf[0], vbase);
+        vt_issue_step<1>(vf[1], vbase);
+        vt_issue_step<2>(vf[2], vbase);
+        PvStep<0, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc);
+      }
+
+      // Flags are double-buffered by tile parity: the write for tile j + 2 happens only
+      // after every wave has passed barrier j + 1, i.e. after it read tile j's slot, so
+      // all waves read the same value and leave the loop on the same tile. A set flag
+      // stays set (it only ever leads to the restart).
+      if (__builtin_amdgcn_ballot_w64(over) != 0) flags[4 * (j & 1) + w] = 1;
+      wait_vm_all();
+      __syncthreads();   // K(j+2), V(j+1) landed; everyone is done with K(j+1) and V(j)
+      if (pass == 0) {
+        // act on the flags of the tile before (one tile late, so the read is off the
+        // critical path; the extra tile's garbage is discarded by the restart)
+        if (flag_seen != 0) {
+          restart = true;
+          break;
+        }
+        const i32x4 f = *reinterpret_cast<const i32x4*>(flags + 4 * (j & 1));
+        flag_seen = f[0] | f[1] | f[2] | f[3];
       }
     }
+    if (pass == 0 && !restart && flag_seen != 0) restart = true;   // raised on the last tile
+    if (!restart) break;
 
-    // ---- P(j), interleaved with S(j+1) = K(j+1) · Q^T ----
-    bf16x8 ph[QB][2], pl[QB][2];
+    // ---- exact column maxima over every visible key (max-only sweep) ----
 #pragma unroll
-    for (int b = 0; b < QB; ++b)
+    for (int b = 0; b < QB; ++b) m[b] = -__builtin_inff();
+    for (int t = 0; t < ntiles; ++t) {
+      copy_k<PAGED, INT8K>(p, g, t * kKt, w, lane, smem, skring);
+      wait_vm_all();
+      __syncthreads();
+      qk_tile(smem_addr);
+      float sc[QB][16], scale[QB];
+      tile_scores(skring, t * kKt, sc, scale);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) sacc[b][kb] = Acc{0, 0, 0, 0};
-    {
-      const uint32_t kn = lds_addr(knext);
-      u32x4 kf[2][4];
-      Q::template issue<0>(kf[0], kn + kb_even, kn + kb_odd);
-      // one (query block, key half) of P per two K steps (per K step with INT8 keys)
-      constexpr int kPer = Q::kSteps / (2 * QB) > 0 ? Q::kSteps / (2 * QB) : 1;
-      auto softmax_part = [&](int st) {
-        if ((st + 1) % kPer == 0 && (st + 1) / kPer <= 2 * QB) {
-          const int idx = (st + 1) / kPer - 1;
-          const int b = idx >> 1, ks = idx & 1;
-          const float nm = -m[b];
-          f32x8 pv;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][8 * ks + e], scale[b], nm));
-          ph[b][ks] = __builtin_convertvector(pv, bf16x8);
-          if constexpr (SPLIT)
-            pl[b][ks] = __builtin_convertvector(pv - __builtin_convertvector(ph[b][ks], f32x8), bf16x8);
-        }
-      };
-      qk_steps<INT8K, QB, 0>(kf, kn + kb_even, kn + kb_odd, qf, sacc, softmax_part);
+      for (int b = 0; b < QB; ++b)
+        m[b] = fmaxf(m[b], xor32_max(xor16_max(lane_max(sc, b))) * scale[b]);
+      __syncthreads();
     }
-
-    // ---- O^T += V^T(j) · P^T(j) ----
-    {
-      uint32_t vbase[4];
-      const uint32_t v0 = lds_addr(vcur);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) vbase[jj] = v0 + vbase_off[jj];
-      VtFrag vf[kVtDepth + 1];
-      vt_issue_step<0>(vf[0], vbase);
-      vt_issue_step<1>(vf[1], vbase);
-      vt_issue_step<2>(vf[2], vbase);
-      PvStep<0, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc);
-    }
-
-    wait_vm_all();
-    __syncthreads();   // K(j+2), V(j+1) landed; everyone is done with K(j+1) and V(j)
   }
 
   // ---- epilogue: O / l -> bf16 ----

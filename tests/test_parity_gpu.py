@@ -249,3 +249,55 @@ def test_long_kv_edge():
     mx, mean = errors(out[torch.from_numpy(rows).to(DEV)], oracle.attention(q, k, v, rows=rows))
     note(f"  max {mx:.3e} mean {mean:.3e}")
     assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+# ------------------------------------------------------------------ reference-maximum restart
+
+def _shift_scores(q, k, start, shift=40.0):
+    """Add `shift` to feature 0 of every query and set feature 0 of keys `start`.. to
+    `shift`: those keys' scores rise by a per-query constant of shift^2 / 16 = 100
+    (144 in log2 units) above the first 64 keys' maximum. Exponentials taken against
+    the first tile's maximum would overflow float32, so only the kernel's restart
+    with exact column maxima gives finite results; the softmax among the risen keys
+    stays as spread as for N(0, 1) data."""
+    q2, k2 = q.to(torch.float32).clone(), k.to(torch.float32).clone()
+    q2[..., 0] += shift
+    k2[start:, :, 0] = shift
+    return q2.to(torch.bfloat16), k2.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("q_len,kv_len,start", [(64, 300, 100), (70, 700, 64), (100, 1200, 300)])
+def test_restart_contiguous(q_len, kv_len, start):
+    note(f"case restart contiguous {q_len}x{kv_len}")
+    q, k, v, _ = make_qkv(q_len, kv_len, seed=4000 + kv_len)
+    q, k = _shift_scores(q, k, start)
+    out = gqa.gqa_attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    mx, mean = errors(out, oracle.attention(q, k, v))
+    note(f"  max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+def test_restart_paged():
+    note("case restart paged")
+    q, k, v, rng = make_qkv(48, 400, seed=4100)
+    q, k = _shift_scores(q, k, 150)
+    bt = block_table_for(rng, 400, 30)
+    kc, vc = scatter_paged(k, bt, 30), scatter_paged(v, bt, 30)
+    out = gqa.gqa_attn_prefill(q.to(DEV), kc.to(DEV), vc.to(DEV), block_table=bt.to(DEV),
+                               kv_len=400)
+    torch.cuda.synchronize()
+    mx, mean = errors(out, oracle.attention(q, k, v))
+    note(f"  max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+def test_restart_int8k():
+    note("case restart int8k")
+    q, k, v, _ = make_qkv(64, 500, seed=4200)
+    q, k = _shift_scores(q, k, 200)
+    kq, ks = oracle.quantize_rows_int8(k)
+    out = gqa.gqa_attn_prefill(q.to(DEV), torch.from_numpy(kq).to(DEV), v.to(DEV),
+                               k_scale=torch.from_numpy(ks).to(DEV))
+    torch.cuda.synchronize()
+    assert int8_excess(out, oracle.attention_int8k(q, kq, ks, v)) <= 0
