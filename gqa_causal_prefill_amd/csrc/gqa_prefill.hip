@@ -242,14 +242,12 @@ struct QK {
   using Frag = typename std::conditional<INT8K, i32x4, bf16x8>::type;
   static constexpr int kSteps = INT8K ? 4 : 8;
 
-  // The 4 fragments (kb = 0..3) of K step s; `base` = the lane's even- or odd-step base.
-  template <int S>
-  static __device__ __forceinline__ void issue(u32x4 (&f)[4], uint32_t base_even, uint32_t base_odd) {
+  // Fragments kb = KB0, KB0 + 1 of K step s; `base` = the lane's even- or odd-step base.
+  template <int S, int KB0>
+  static __device__ __forceinline__ void issue(u32x4 (&f)[2], uint32_t base_even, uint32_t base_odd) {
     const uint32_t base = (S & 1) ? base_odd : base_even;
-    f[0] = lds_read_b128<(S >> 1) * kSegStride + 0 * 2048>(base);
-    f[1] = lds_read_b128<(S >> 1) * kSegStride + 1 * 2048>(base);
-    f[2] = lds_read_b128<(S >> 1) * kSegStride + 2 * 2048>(base);
-    f[3] = lds_read_b128<(S >> 1) * kSegStride + 3 * 2048>(base);
+    f[0] = lds_read_b128<(S >> 1) * kSegStride + (KB0 + 0) * 2048>(base);
+    f[1] = lds_read_b128<(S >> 1) * kSegStride + (KB0 + 1) * 2048>(base);
   }
 
   static __device__ __forceinline__ Acc mfma(const u32x4& k, const Frag& q, const Acc& c) {
@@ -260,25 +258,43 @@ struct QK {
   }
 };
 
-// One K step: wait for its fragments (the next step's 4 reads may stay in flight),
-// issue the reads of step S + 1, run the 4 x QB MFMAs of step S, then `extra(S)`.
-template <bool INT8K, int QB, int S, class Extra>
-__device__ __forceinline__ void qk_steps(u32x4 (&kf)[2][4], uint32_t be, uint32_t bo,
-                                         const typename QK<INT8K, QB>::Frag (&qf)[QB][QK<INT8K, QB>::kSteps],
-                                         typename QK<INT8K, QB>::Acc (&acc)[QB][4], Extra&& extra) {
+template <int N>
+__device__ __forceinline__ void lds_wait2(u32x4& a, u32x4& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+
+// One K step S over key blocks KB0, KB0 + 1 (32 keys): wait for its 2 fragments
+// (the next step's 2 reads may stay in flight), issue the reads of step S + 1, run
+// its 2 x QB MFMAs, then `extra(S)`.
+template <bool INT8K, int QB, int KB0, int S, class Extra>
+__device__ __forceinline__ void qk_half(u32x4 (&kf)[2][2], uint32_t be, uint32_t bo,
+                                        const typename QK<INT8K, QB>::Frag (&qf)[QB][QK<INT8K, QB>::kSteps],
+                                        typename QK<INT8K, QB>::Acc (&acc)[QB][4], Extra&& extra) {
   using Q = QK<INT8K, QB>;
   if constexpr (S + 1 < Q::kSteps) {
-    Q::template issue<S + 1>(kf[(S + 1) & 1], be, bo);
-    lds_wait4<4>(kf[S & 1][0], kf[S & 1][1], kf[S & 1][2], kf[S & 1][3]);
+    Q::template issue<S + 1, KB0>(kf[(S + 1) & 1], be, bo);
+    lds_wait2<2>(kf[S & 1][0], kf[S & 1][1]);
   } else {
-    lds_wait4<0>(kf[S & 1][0], kf[S & 1][1], kf[S & 1][2], kf[S & 1][3]);
+    lds_wait2<0>(kf[S & 1][0], kf[S & 1][1]);
   }
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int b = 0; b < QB; ++b) acc[b][kb] = Q::mfma(kf[S & 1][kb], qf[b][S], acc[b][kb]);
+    for (int b = 0; b < QB; ++b)
+      acc[b][KB0 + kk] = Q::mfma(kf[S & 1][kk], qf[b][S], acc[b][KB0 + kk]);
   extra(S);
-  if constexpr (S + 1 < Q::kSteps) qk_steps<INT8K, QB, S + 1>(kf, be, bo, qf, acc, extra);
+  if constexpr (S + 1 < Q::kSteps) qk_half<INT8K, QB, KB0, S + 1>(kf, be, bo, qf, acc, extra);
+}
+
+// All K steps over key blocks KB0, KB0 + 1 of the tile at LDS address `kbuf`.
+template <bool INT8K, int QB, int KB0, class Extra>
+__device__ __forceinline__ void qk_pair(uint32_t kbuf, int kb_even, int kb_odd,
+                                        const typename QK<INT8K, QB>::Frag (&qf)[QB][QK<INT8K, QB>::kSteps],
+                                        typename QK<INT8K, QB>::Acc (&acc)[QB][4], Extra&& extra) {
+  using Q = QK<INT8K, QB>;
+  u32x4 kf[2][2];
+  Q::template issue<0, KB0>(kf[0], kbuf + kb_even, kbuf + kb_odd);
+  qk_half<INT8K, QB, KB0, 0>(kf, kbuf + kb_even, kbuf + kb_odd, qf, acc, extra);
 }
 
 // ---- O^T += V^T · P^T (and l += 1 · P^T) ----
@@ -496,61 +512,73 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     for (int b = 0; b < QB; ++b)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) sacc[b][kb] = Acc{0, 0, 0, 0};
-    u32x4 kf[2][4];
-    Q::template issue<0>(kf[0], kbuf + kb_even, kbuf + kb_odd);
-    qk_steps<INT8K, QB, 0>(kf, kbuf + kb_even, kbuf + kb_odd, qf, sacc, [](int) {});
+    qk_pair<INT8K, QB, 0>(kbuf, kb_even, kb_odd, qf, sacc, [](int) {});
+    qk_pair<INT8K, QB, 2>(kbuf, kb_even, kb_odd, qf, sacc, [](int) {});
   };
-  // scores of the tile at kbase from sacc, in log2 units once multiplied by scale[b]
-  // (bf16: raw dot products; INT8 keys: already scaled), causal mask applied
-  auto tile_scores = [&](const float* sk, int kbase, float (&sc)[QB][16], float (&scale)[QB]) {
+  // scores of key blocks 2h, 2h + 1 (keys kbase + 32 h .. + 31) from sacc, in log2 units
+  // once multiplied by scale[b] (bf16: raw dot products; INT8 keys: already scaled),
+  // causal mask applied. sc[b][e]: e = 0..3 keys 32 h + 4 L + e, e = 4..7 keys 32 h + 16 + 4 L + e - 4
+  auto half_scores = [&](const float* sk, int kbase, int h, float (&sc)[QB][8], float (&scale)[QB]) {
     if constexpr (!INT8K) {
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
         scale[b] = kLog2eOver16;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sc[b][4 * kb + r] = sacc[b][kb][r];
+          for (int r = 0; r < 4; ++r) sc[b][4 * kk + r] = sacc[b][2 * h + kk][r];
       }
     } else {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const f32x4 skv = *reinterpret_cast<const f32x4*>(sk + 16 * kb + 4 * L);
+      for (int kk = 0; kk < 2; ++kk) {
+        const f32x4 skv = *reinterpret_cast<const f32x4*>(sk + 16 * (2 * h + kk) + 4 * L);
 #pragma unroll
         for (int b = 0; b < QB; ++b)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sc[b][4 * kb + r] = (float)sacc[b][kb][r] * (skv[r] * qs[b]);
+          for (int r = 0; r < 4; ++r)
+            sc[b][4 * kk + r] = (float)sacc[b][2 * h + kk][r] * (skv[r] * qs[b]);
       }
 #pragma unroll
       for (int b = 0; b < QB; ++b) scale[b] = 1.0f;
     }
     if (kbase + kKt - 1 > off + t0) {   // only tiles that reach past the workgroup's first query
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = kbase + 16 * kb + 4 * L + r;
+          const int key = kbase + 16 * (2 * h + kk) + 4 * L + r;
           if (key > limit) {
 #pragma unroll
-            for (int b = 0; b < QB; ++b) sc[b][4 * kb + r] = -__builtin_inff();
+            for (int b = 0; b < QB; ++b) sc[b][4 * kk + r] = -__builtin_inff();
           }
         }
     }
   };
   // this lane's maximum of each column (not yet reduced over the 4 lanes of a column)
-  auto lane_max = [&](const float (&sc)[QB][16], int b) {
+  auto lane_max = [&](const float (&sc)[QB][8], int b) {
     float mx = sc[b][0];
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[b][e]);
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[b][e]);
     return mx;
+  };
+  // column maxima of the whole tile in sacc (reduced over the 4 lanes of a column)
+  auto tile_max = [&](const float* sk, int kbase, float (&mx)[QB]) {
+    float sc0[QB][8], sc1[QB][8], scale[QB];
+    half_scores(sk, kbase, 0, sc0, scale);
+    half_scores(sk, kbase, 1, sc1, scale);
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+      mx[b] = xor32_max(xor16_max(fmaxf(lane_max(sc0, b), lane_max(sc1, b)))) * scale[b];
   };
 
   // Pass 0 takes each column's maximum over tile 0 as the reference and checks every
   // later tile against it: a score more than 2^kTau above the reference makes the
   // whole workgroup start again (pass 1) with the exact column maxima over all its
   // keys, found by a max-only sweep. Either way no accumulator is ever rescaled.
-  for (int pass = 0;; ++pass) {
-    if (pass > 0) {
+  // (two instantiations, not a loop, so nothing of pass 1 is hoisted into pass 0)
+  auto main_pass = [&](auto pass_c) -> bool {
+    constexpr int pass = decltype(pass_c)::value;
+    if constexpr (pass > 0) {
       copy_k<PAGED, INT8K>(p, g, 0, w, lane, smem, skring);
       copy_v<PAGED>(p, g, 0, w, lane, smem + kVOff);
       if (ntiles > 1) copy_k<PAGED, INT8K>(p, g, kKt, w, lane, smem + kKTile, skring + kKt);
@@ -565,12 +593,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     wait_vm_all();
     __syncthreads();
     qk_tile(smem_addr);   // S(0)
-    if (pass == 0) {
-      float sc[QB][16], scale[QB];
-      tile_scores(skring, 0, sc, scale);
-#pragma unroll
-      for (int b = 0; b < QB; ++b) m[b] = xor32_max(xor16_max(lane_max(sc, b))) * scale[b];
-    }
+    if (pass == 0) tile_max(skring, 0, m);
     __syncthreads();   // every wave is done with K(0) before K(2) overwrites it
 
     bool restart = false;
@@ -585,42 +608,42 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       if (j + 1 < ntiles)
         copy_v<PAGED>(p, g, kbase + kKt, w, lane, smem + kVOff + ((j + 1) & 1) * 4 * kSegStride);
 
-      float sc[QB][16], scale[QB];
-      tile_scores(skring + (j % 3) * kKt, kbase, sc, scale);
-      bool over = false;
-      if (pass == 0) {
-#pragma unroll
-        for (int b = 0; b < QB; ++b) over = over || (lane_max(sc, b) * scale[b] > m[b] + kTau);
-      }
-
-      // ---- P(j), interleaved with S(j+1) = K(j+1) · Q^T ----
+      // ---- P(j) from S(j), interleaved with S(j+1) = K(j+1) · Q^T, one 32-key half at a
+      // time: the half of S(j) being turned into P is copied out of the accumulators
+      // before the MFMAs of S(j+1) overwrite them ----
       bf16x8 ph[QB][2], pl[QB][2];
+      bool over = false;
+      const uint32_t kn = lds_addr(knext);
+      auto half = [&](auto hc) {
+        constexpr int H = decltype(hc)::value;
+        float sc[QB][8], scale[QB];
+        half_scores(skring + (j % 3) * kKt, kbase, H, sc, scale);
+        if (pass == 0) {
 #pragma unroll
-      for (int b = 0; b < QB; ++b)
+          for (int b = 0; b < QB; ++b) over = over || (lane_max(sc, b) * scale[b] > m[b] + kTau);
+        }
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) sacc[b][kb] = Acc{0, 0, 0, 0};
-      {
-        const uint32_t kn = lds_addr(knext);
-        u32x4 kf[2][4];
-        Q::template issue<0>(kf[0], kn + kb_even, kn + kb_odd);
-        // one (query block, key half) of P per two K steps (per K step with INT8 keys)
-        constexpr int kPer = Q::kSteps / (2 * QB) > 0 ? Q::kSteps / (2 * QB) : 1;
+        for (int b = 0; b < QB; ++b) sacc[b][2 * H] = sacc[b][2 * H + 1] = Acc{0, 0, 0, 0};
+        // P for query block b after K step ((b + 1) * steps) / QB - 1 of this half
         auto softmax_part = [&](int st) {
-          if ((st + 1) % kPer == 0 && (st + 1) / kPer <= 2 * QB) {
-            const int idx = (st + 1) / kPer - 1;
-            const int b = idx >> 1, ks = idx & 1;
-            const float nm = -m[b];
-            f32x8 pv;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][8 * ks + e], scale[b], nm));
-            ph[b][ks] = __builtin_convertvector(pv, bf16x8);
-            if constexpr (SPLIT)
-              pl[b][ks] = __builtin_convertvector(pv - __builtin_convertvector(ph[b][ks], f32x8), bf16x8);
+          for (int b = 0; b < QB; ++b) {
+            if (st == ((b + 1) * Q::kSteps) / QB - 1) {
+              const float nm = -m[b];
+              f32x8 pv;
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][e], scale[b], nm));
+              ph[b][H] = __builtin_convertvector(pv, bf16x8);
+              if constexpr (SPLIT)
+                pl[b][H] = __builtin_convertvector(pv - __builtin_convertvector(ph[b][H], f32x8), bf16x8);
+            }
           }
         };
-        qk_steps<INT8K, QB, 0>(kf, kn + kb_even, kn + kb_odd, qf, sacc, softmax_part);
-      }
+        qk_pair<INT8K, QB, 2 * H>(kn, kb_even, kb_odd, qf, sacc, softmax_part);
+      };
+      half(std::integral_constant<int, 0>{});
+      half(std::integral_constant<int, 1>{});
 
       // ---- O^T += V^T(j) · P^T(j) ----
       {
@@ -654,9 +677,11 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       }
     }
     if (pass == 0 && !restart && flag_seen != 0) restart = true;   // raised on the last tile
-    if (!restart) break;
+    return restart;
+  };
 
-    // ---- exact column maxima over every visible key (max-only sweep) ----
+  if (main_pass(std::integral_constant<int, 0>{})) {
+    // ---- exact column maxima over every visible key (max-only sweep), then pass 1 ----
 #pragma unroll
     for (int b = 0; b < QB; ++b) m[b] = -__builtin_inff();
     for (int t = 0; t < ntiles; ++t) {
@@ -664,13 +689,13 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       wait_vm_all();
       __syncthreads();
       qk_tile(smem_addr);
-      float sc[QB][16], scale[QB];
-      tile_scores(skring, t * kKt, sc, scale);
+      float mx[QB];
+      tile_max(skring, t * kKt, mx);
 #pragma unroll
-      for (int b = 0; b < QB; ++b)
-        m[b] = fmaxf(m[b], xor32_max(xor16_max(lane_max(sc, b))) * scale[b]);
+      for (int b = 0; b < QB; ++b) m[b] = fmaxf(m[b], mx[b]);
       __syncthreads();
     }
+    main_pass(std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: O / l -> bf16 ----
