@@ -63,7 +63,11 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKt = 64;                  // keys per KV tile
 constexpr int kSplitBelow = 256;
-constexpr float kTau = 32.0f;   // log2 headroom of the reference maximum
+// Pass 0 restarts once a column's running sum of exponentials exceeds 2^32: every
+// exponential is then still at most 2^32 (finite in bf16 and fp32 with ample margin
+// for the fp32 accumulation of up to 2^24 keys), and a sum that overflowed is inf,
+// which compares greater too.
+constexpr float kOverSum = 4294967296.0f;
 constexpr float kLog2eOver16 = 1.4426950408889634f / 16.0f;
 
 constexpr int kSkTile = kKt * 4;         // 256 B of key scales per tile
@@ -138,15 +142,18 @@ __device__ __forceinline__ size_t kv_row(int g, int key, int blk) {
 // with `piece` the 16-byte piece index inside the row and a per-tensor XOR swizzle
 //   K: swz = key & 7         (the 8 lanes of a ds_read_b128 phase read 8 keys at one
 //                             piece and hit 8 different 16-byte bank groups)
-//   V: swz = (key & 3) << 1  (the 4 keys of one 16-lane transposing read land in 4
-//                             different 32-byte bank groups)
+//   V: swz = ((key >> 1) & 3) << 1
+//                            (a transposing read serves 32 lanes per LDS cycle: 8 keys
+//                             x 32 bytes; keys of equal parity share the 128-byte half
+//                             of the 256-byte bank row and this swizzle spreads the
+//                             four of each parity over its four 32-byte bank groups)
 // A global->LDS copy instruction moves 8 keys x one 128-byte segment: every lane
 // group of 8 reads one whole 128-byte line of a key row.
 constexpr int kSegStride = kKt * 128;   // 8 KiB
 
 template <bool V>
 __device__ __forceinline__ int tile_swizzle(int key) {
-  return V ? ((key & 3) << 1) : (key & 7);
+  return V ? (((key >> 1) & 3) << 1) : (key & 7);
 }
 
 // Copy this wave's 16 keys (keys 16w .. 16w + 15 of the tile at kbase) of one
@@ -490,9 +497,10 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   const int kb_even = c * 128 + ((L ^ (c & 7)) << 4);
   const int kb_odd = c * 128 + (((L ^ (c & 7)) ^ 4) << 4);
   uint32_t vbase_off[4];
+  const int vsw = tile_swizzle<true>(4 * L + (c >> 2)) >> 1;   // V swizzle of this lane's key
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj)
-    vbase_off[jj] = (4 * L + (c >> 2)) * 128 + ((2 * (jj ^ (c >> 2)) + ((c & 3) >> 1)) << 4) +
+    vbase_off[jj] = (4 * L + (c >> 2)) * 128 + ((2 * (jj ^ vsw) + ((c & 3) >> 1)) << 4) +
                     8 * (c & 1);
   bf16x8 ones;
 #pragma unroll
@@ -571,10 +579,12 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       mx[b] = xor32_max(xor16_max(fmaxf(lane_max(sc0, b), lane_max(sc1, b)))) * scale[b];
   };
 
-  // Pass 0 takes each column's maximum over tile 0 as the reference and checks every
-  // later tile against it: a score more than 2^kTau above the reference makes the
-  // whole workgroup start again (pass 1) with the exact column maxima over all its
-  // keys, found by a max-only sweep. Either way no accumulator is ever rescaled.
+  // Pass 0 takes each column's maximum over tile 0 as the reference (tile 0 holds key
+  // 0, which every query sees, so the reference is a real score of the column and its
+  // sum of exponentials is at least 1). If a column's running sum exceeds kOverSum
+  // (some later score lies far above the reference) the whole workgroup starts again
+  // (pass 1) with the exact column maxima over all its keys, found by a max-only
+  // sweep. Either way no accumulator is ever rescaled.
   // (two instantiations, not a loop, so nothing of pass 1 is hoisted into pass 0)
   auto main_pass = [&](auto pass_c) -> bool {
     constexpr int pass = decltype(pass_c)::value;
@@ -618,10 +628,6 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
         constexpr int H = decltype(hc)::value;
         float sc[QB][8], scale[QB];
         half_scores(skring + (j % 3) * kKt, kbase, H, sc, scale);
-        if (pass == 0) {
-#pragma unroll
-          for (int b = 0; b < QB; ++b) over = over || (lane_max(sc, b) * scale[b] > m[b] + kTau);
-        }
 #pragma unroll
         for (int b = 0; b < QB; ++b) sacc[b][2 * H] = sacc[b][2 * H + 1] = Acc{0, 0, 0, 0};
         // P for query block b after K step ((b + 1) * steps) / QB - 1 of this half
@@ -662,7 +668,11 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       // after every wave has passed barrier j + 1, i.e. after it read tile j's slot, so
       // all waves read the same value and leave the loop on the same tile. A set flag
       // stays set (it only ever leads to the restart).
-      if (__builtin_amdgcn_ballot_w64(over) != 0) flags[4 * (j & 1) + w] = 1;
+      if (pass == 0) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b) over = over || !(lacc[b][0] <= kOverSum);
+        if (__builtin_amdgcn_ballot_w64(over) != 0) flags[4 * (j & 1) + w] = 1;
+      }
       wait_vm_all();
       __syncthreads();   // K(j+2), V(j+1) landed; everyone is done with K(j+1) and V(j)
       if (pass == 0) {
