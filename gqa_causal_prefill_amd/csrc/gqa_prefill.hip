@@ -70,7 +70,7 @@ constexpr int kSplitBelow = 256;
 constexpr float kOverSum = 4294967296.0f;
 constexpr float kLog2eOver16 = 1.4426950408889634f / 16.0f;
 
-constexpr int kSkTile = kKt * 4;         // 256 B of key scales per tile
+constexpr int kSkTile = kKt * kHkv * 4;  // 1 KiB of key scales per tile (all KV heads)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -156,61 +156,91 @@ __device__ __forceinline__ int tile_swizzle(int key) {
   return V ? (((key >> 1) & 3) << 1) : (key & 7);
 }
 
-// Copy this wave's 16 keys (keys 16w .. 16w + 15 of the tile at kbase) of one
-// tensor into an LDS tile. Keys past kv_len are clamped to the last key: finite
-// duplicates that the causal mask hides. The wave's 16 keys lie in one 16-key block,
-// so the source is a wave-uniform base (the wave's first row, or its physical block)
-// plus a small per-lane offset. `w` is wave-uniform.
-template <bool PAGED, bool V, int NSEG>
-__device__ __forceinline__ void copy_rows(const Params& p, const uint8_t* base, int elem_bytes,
-                                          int g, int kbase, int w, int lane, uint8_t* tile) {
-  const int kr = lane >> 3;   // key within an 8-key group
-  const int pp = lane & 7;    // physical piece within the 128-byte segment
-  const int row_bytes = kD * elem_bytes;
-  const int first = min(kbase + 16 * w, p.kv_len - 1);   // wave-uniform
-  const uint8_t* wbase;
-  if constexpr (PAGED) {
-    const int blk = min(max(p.bt[first >> 4], 0), p.num_blocks - 1);
-    wbase = base + ((size_t)(blk * kHkv + g) * kBs) * row_bytes;
-  } else {
-    wbase = base + ((size_t)first * kHkv + g) * row_bytes;
-  }
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int slot = 16 * w + 8 * half + kr;            // key slot in the tile
-    const int key = min(kbase + slot, p.kv_len - 1);
-    const int piece = pp ^ tile_swizzle<V>(slot);
-    uint32_t voff;
-    if constexpr (PAGED)
-      voff = (uint32_t)((key & (kBs - 1)) * row_bytes + piece * 16);
-    else
-      voff = (uint32_t)((key - first) * (kHkv * row_bytes) + piece * 16);
-    uint8_t* dst = tile + (16 * w + 8 * half) * 128;
-#pragma unroll
-    for (int sg = 0; sg < NSEG; ++sg) {
-      const uint8_t* sbase = wbase + sg * 128;   // uniform: the segment step stays scalar
-      __builtin_amdgcn_global_load_lds(sbase + voff, dst + sg * kSegStride, 16, 0, 0);
-    }
+// ---- global -> LDS tile copies ----
+// Each wave copies its 16 keys (keys 16w .. 16w + 15 of a tile) of a tensor with
+// buffer loads that write LDS directly. The wave's keys lie in one 16-key block, so a
+// wave-uniform buffer descriptor starts at its first row (or its physical block) and
+// every lane offset is a constant of the kernel. The descriptor's size ends right
+// after the last row before kv_len: rows past it are out of range, and such buffer
+// loads write zeros into LDS (finite rows that the causal mask hides). A tile past the
+// end therefore costs no memory traffic at all.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// f(std::integral_constant<int, I>) for I = LO .. HI - 1
+template <int LO, int HI, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (LO < HI) {
+    f(std::integral_constant<int, LO>{});
+    static_for<LO + 1, HI>(f);
   }
 }
 
-template <bool PAGED, bool INT8K>
-__device__ __forceinline__ void copy_k(const Params& p, int g, int kbase, int w, int lane,
-                                       uint8_t* ktile, float* sk) {
-  copy_rows<PAGED, false, INT8K ? 2 : 4>(p, p.k, INT8K ? 1 : 2, g, kbase, w, lane, ktile);
-  if constexpr (INT8K) {
-    if (w == 0) {
-      const int key = min(kbase + lane, p.kv_len - 1);
-      __builtin_amdgcn_global_load_lds(p.ks + (size_t)key * kHkv + g, sk, 4, 0, 0);
-    }
-  }
+__device__ __forceinline__ lds_void* lds_ptr(uint32_t addr) {
+  return (lds_void*)(uintptr_t)addr;
 }
 
-template <bool PAGED>
-__device__ __forceinline__ void copy_v(const Params& p, int g, int kbase, int w, int lane,
-                                       uint8_t* vtile) {
-  copy_rows<PAGED, true, 4>(p, p.v, 2, g, kbase, w, lane, vtile);
-}
+template <bool PAGED, int ROW_BYTES, bool V>
+struct WaveCopy {
+  static constexpr int kNseg = ROW_BYTES / 128;                      // 128-byte segments per row
+  static constexpr int kInsts = 2 * kNseg;                          // 8 keys x one segment each
+  static constexpr int kStride = PAGED ? ROW_BYTES : kHkv * ROW_BYTES;   // bytes between keys
+
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t lds;   // LDS address of the wave's first row, segment 0, in the destination tile
+
+  // Source offset of lane (kr = lane / 8, physical piece pp = lane % 8) for key half `half`:
+  // the lane fetches the logical piece that the tile swizzle stores at position pp.
+  static __device__ __forceinline__ uint32_t lane_offset(int lane, int half) {
+    const int kr = lane >> 3, pp = lane & 7;
+    return (uint32_t)((8 * half + kr) * kStride + ((pp ^ tile_swizzle<V>(kr)) << 4));
+  }
+
+  // first = kbase + 16 w (wave-uniform); lds_rows = destination tile + 16 w rows
+  __device__ __forceinline__ WaveCopy(const Params& p, const uint8_t* base, int g, int first,
+                                      uint32_t lds_rows) {
+    const int n = min(max(p.kv_len - first, 0), 16);   // rows of this wave before kv_len
+    // (uniform; readfirstlane keeps the whole descriptor in scalar registers)
+    const int nrec = __builtin_amdgcn_readfirstlane(n > 0 ? (n - 1) * kStride + ROW_BYTES : 0);
+    const uint8_t* wb;
+    if constexpr (PAGED) {
+      const int blk = min(max(p.bt[min(first, p.kv_len - 1) >> 4], 0), p.num_blocks - 1);
+      wb = base + (size_t)(blk * kHkv + g) * kBs * ROW_BYTES;
+    } else {
+      wb = base + ((size_t)first * kHkv + g) * ROW_BYTES;   // not dereferenced when n == 0
+    }
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wb), (short)0, nrec, 0x00020000);
+    lds = lds_rows;
+  }
+
+  // Instruction I: key half I / kNseg, segment I % kNseg.
+  template <int I>
+  __device__ __forceinline__ void issue(const uint32_t (&voff)[2]) const {
+    constexpr int half = I / kNseg, sg = I % kNseg;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds + half * 1024 + sg * kSegStride), 16,
+                                             voff[half], sg * 128, 0, 0);
+  }
+};
+
+// INT8 key scales: each wave copies the scales of its 16 keys for all 4 KV heads into
+// a 1 KiB slot laid out [16-key block][KV head][16 keys] (lane = 16 head + key).
+struct ScaleCopy {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t lds;
+  __device__ __forceinline__ ScaleCopy() = default;
+  static __device__ __forceinline__ uint32_t lane_offset(int lane) {
+    return (uint32_t)((lane & 15) * kHkv * 4 + (lane >> 4) * 4);
+  }
+  __device__ __forceinline__ ScaleCopy(const Params& p, int first, uint32_t lds_block) {
+    const int n = min(max(p.kv_len - first, 0), 16);
+    const uint8_t* wb = reinterpret_cast<const uint8_t*>(p.ks) + (size_t)first * kHkv * 4;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wb), (short)0,
+                                             __builtin_amdgcn_readfirstlane(n * kHkv * 4), 0x00020000);
+    lds = lds_block;
+  }
+  __device__ __forceinline__ void issue(uint32_t voff) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds), 4, voff, 0, 0, 0);
+  }
+};
 
 __device__ __forceinline__ void wait_vm_all() {
   // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
@@ -289,7 +319,7 @@ __device__ __forceinline__ void qk_half(u32x4 (&kf)[2][2], uint32_t be, uint32_t
 #pragma unroll
     for (int b = 0; b < QB; ++b)
       acc[b][KB0 + kk] = Q::mfma(kf[S & 1][kk], qf[b][S], acc[b][KB0 + kk]);
-  extra(S);
+  extra(std::integral_constant<int, S>{});
   if constexpr (S + 1 < Q::kSteps) qk_half<INT8K, QB, KB0, S + 1>(kf, be, bo, qf, acc, extra);
 }
 
@@ -401,8 +431,6 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   constexpr int kVOff = 2 * kKTile;                    // V tiles follow the two K tiles
   constexpr int kSkOff = kVOff + 8 * kSegStride;       // then the key-scale ring
   constexpr int kFlagOff = kSkOff + (INT8K ? 3 * kSkTile : 0);   // then the restart flags
-  // (buffers are addressed as smem + offset so every access stays an LDS access)
-  float* const skring = reinterpret_cast<float*>(smem + kSkOff);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -432,10 +460,38 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   const int last_tok = min(t0 + S::kTokPerWg, p.q_len);
   const int ntiles = (off + last_tok + kKt - 1) / kKt;
 
+  // ---- tile copies (this wave's 16 keys of each tile) ----
+  using KCopy = WaveCopy<PAGED, INT8K ? kD : 2 * kD, false>;
+  using VCopy = WaveCopy<PAGED, 2 * kD, true>;
+  const uint32_t smem_addr = lds_addr(smem);
+  const uint32_t sk_addr = smem_addr + kSkOff;   // key-scale ring (INT8 keys)
+  const uint32_t kvo[2] = {KCopy::lane_offset(lane, 0), KCopy::lane_offset(lane, 1)};
+  const uint32_t vvo[2] = {VCopy::lane_offset(lane, 0), VCopy::lane_offset(lane, 1)};
+  const uint32_t svo = ScaleCopy::lane_offset(lane);
+  auto kcopy = [&](int kbase, int buf) {
+    return KCopy(p, p.k, g, kbase + 16 * w, smem_addr + buf * kKTile + 16 * w * 128);
+  };
+  auto vcopy = [&](int kbase, int buf) {
+    return VCopy(p, p.v, g, kbase + 16 * w, smem_addr + kVOff + buf * 4 * kSegStride + 16 * w * 128);
+  };
+  auto scopy = [&](int kbase, int slot) {
+    return ScaleCopy(p, kbase + 16 * w, sk_addr + slot * kSkTile + w * 256);
+  };
+  // whole-tile copies outside the pipelined loop
+  auto copy_k_all = [&](int kbase, int buf, int slot) {
+    const KCopy kc = kcopy(kbase, buf);
+    static_for<0, KCopy::kInsts>([&](auto ic) { kc.template issue<decltype(ic)::value>(kvo); });
+    if constexpr (INT8K) scopy(kbase, slot).issue(svo);
+  };
+  auto copy_v_all = [&](int kbase, int buf) {
+    const VCopy vc = vcopy(kbase, buf);
+    static_for<0, VCopy::kInsts>([&](auto ic) { vc.template issue<decltype(ic)::value>(vvo); });
+  };
+
   // start the first copies before the Q prologue
-  copy_k<PAGED, INT8K>(p, g, 0, w, lane, smem, skring);
-  copy_v<PAGED>(p, g, 0, w, lane, smem + kVOff);
-  if (ntiles > 1) copy_k<PAGED, INT8K>(p, g, kKt, w, lane, smem + kKTile, skring + kKt);
+  copy_k_all(0, 0, 0);
+  copy_v_all(0, 0);
+  if (ntiles > 1) copy_k_all(kKt, 1, 1);
 
   // ---- prologue: Q fragments (B operand of S^T = K·Q^T) ----
   typename Q::Frag qf[QB][Q::kSteps];
@@ -511,7 +567,6 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   f32x4 lacc[QB];
   float m[QB];   // reference maximum per column (log2 units), fixed during a pass
   Acc sacc[QB][4];
-  const uint32_t smem_addr = lds_addr(smem);
   int* const flags = reinterpret_cast<int*>(smem + kFlagOff);
 
   // S^T of the tile in K buffer `kbuf` into sacc
@@ -520,13 +575,15 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     for (int b = 0; b < QB; ++b)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) sacc[b][kb] = Acc{0, 0, 0, 0};
-    qk_pair<INT8K, QB, 0>(kbuf, kb_even, kb_odd, qf, sacc, [](int) {});
-    qk_pair<INT8K, QB, 2>(kbuf, kb_even, kb_odd, qf, sacc, [](int) {});
+    qk_pair<INT8K, QB, 0>(kbuf, kb_even, kb_odd, qf, sacc, [](auto) {});
+    qk_pair<INT8K, QB, 2>(kbuf, kb_even, kb_odd, qf, sacc, [](auto) {});
   };
   // scores of key blocks 2h, 2h + 1 (keys kbase + 32 h .. + 31) from sacc, in log2 units
   // once multiplied by scale[b] (bf16: raw dot products; INT8 keys: already scaled),
   // causal mask applied. sc[b][e]: e = 0..3 keys 32 h + 4 L + e, e = 4..7 keys 32 h + 16 + 4 L + e - 4
-  auto half_scores = [&](const float* sk, int kbase, int h, float (&sc)[QB][8], float (&scale)[QB]) {
+  auto half_scores = [&](auto mask_c, uint32_t sk_slot, int kbase, int h, float (&sc)[QB][8],
+                         float (&scale)[QB]) {
+    constexpr bool kMask = decltype(mask_c)::value;
     if constexpr (!INT8K) {
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
@@ -537,9 +594,15 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
           for (int r = 0; r < 4; ++r) sc[b][4 * kk + r] = sacc[b][2 * h + kk][r];
       }
     } else {
+      // scales of keys 16 (2 h + kk) + 4 L .. + 3 for KV head g
+      u32x4 sr[2];
+      const uint32_t a = sk_slot + 2 * h * 256 + g * 64 + 16 * L;
+      sr[0] = lds_read_b128<0>(a);
+      sr[1] = lds_read_b128<256>(a);
+      lds_wait2<0>(sr[0], sr[1]);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const f32x4 skv = *reinterpret_cast<const f32x4*>(sk + 16 * (2 * h + kk) + 4 * L);
+        const f32x4 skv = __builtin_bit_cast(f32x4, sr[kk]);
 #pragma unroll
         for (int b = 0; b < QB; ++b)
 #pragma unroll
@@ -549,7 +612,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
 #pragma unroll
       for (int b = 0; b < QB; ++b) scale[b] = 1.0f;
     }
-    if (kbase + kKt - 1 > off + t0) {   // only tiles that reach past the workgroup's first query
+    if constexpr (kMask) {   // tiles that reach past the workgroup's first query
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -570,10 +633,10 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     return mx;
   };
   // column maxima of the whole tile in sacc (reduced over the 4 lanes of a column)
-  auto tile_max = [&](const float* sk, int kbase, float (&mx)[QB]) {
+  auto tile_max = [&](uint32_t sk_slot, int kbase, float (&mx)[QB]) {
     float sc0[QB][8], sc1[QB][8], scale[QB];
-    half_scores(sk, kbase, 0, sc0, scale);
-    half_scores(sk, kbase, 1, sc1, scale);
+    half_scores(std::true_type{}, sk_slot, kbase, 0, sc0, scale);
+    half_scores(std::true_type{}, sk_slot, kbase, 1, sc1, scale);
 #pragma unroll
     for (int b = 0; b < QB; ++b)
       mx[b] = xor32_max(xor16_max(fmaxf(lane_max(sc0, b), lane_max(sc1, b)))) * scale[b];
@@ -589,9 +652,9 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   auto main_pass = [&](auto pass_c) -> bool {
     constexpr int pass = decltype(pass_c)::value;
     if constexpr (pass > 0) {
-      copy_k<PAGED, INT8K>(p, g, 0, w, lane, smem, skring);
-      copy_v<PAGED>(p, g, 0, w, lane, smem + kVOff);
-      if (ntiles > 1) copy_k<PAGED, INT8K>(p, g, kKt, w, lane, smem + kKTile, skring + kKt);
+      copy_k_all(0, 0, 0);
+      copy_v_all(0, 0);
+      if (ntiles > 1) copy_k_all(kKt, 1, 1);
     }
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
@@ -603,35 +666,53 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     wait_vm_all();
     __syncthreads();
     qk_tile(smem_addr);   // S(0)
-    if (pass == 0) tile_max(skring, 0, m);
+    if (pass == 0) tile_max(sk_addr, 0, m);
     __syncthreads();   // every wave is done with K(0) before K(2) overwrites it
 
-    bool restart = false;
+    // Tiles that end at or before the workgroup's first query need no causal mask; the
+    // rest (one or two per workgroup) run the masked form of the same body. The body
+    // is one basic block: copies past the last tile re-read the clamped last key into a
+    // buffer nothing reads again, and the restart flag is rewritten every tile.
+    const int n_plain = min(ntiles, (off + t0 + 1) / kKt);
     int flag_seen = 0;   // flags read after the previous tile's barrier
-    for (int j = 0; j < ntiles; ++j) {
+    // returns true when pass 0 must restart
+    auto body = [&](int j, auto mask_c) -> bool {
       const int kbase = j * kKt;
       const uint8_t* knext = smem + ((j + 1) & 1) * kKTile;             // K(j+1) (stale on the last tile)
       const uint8_t* vcur = smem + kVOff + (j & 1) * 4 * kSegStride;   // V(j)
-      if (j + 2 < ntiles)
-        copy_k<PAGED, INT8K>(p, g, kbase + 2 * kKt, w, lane, smem + (j & 1) * kKTile,
-                             skring + ((j + 2) % 3) * kKt);
-      if (j + 1 < ntiles)
-        copy_v<PAGED>(p, g, kbase + kKt, w, lane, smem + kVOff + ((j + 1) & 1) * 4 * kSegStride);
+      // copies of K(j+2) and V(j+1), spread over the K steps of the first half so their
+      // issue hides under the MFMAs
+      const KCopy kc = kcopy(kbase + 2 * kKt, j & 1);
+      const VCopy vc = vcopy(kbase + kKt, (j + 1) & 1);
+      ScaleCopy scp;
+      if constexpr (INT8K) scp = scopy(kbase + 2 * kKt, (j + 2) % 3);
+      constexpr int kCopies = KCopy::kInsts + VCopy::kInsts + (INT8K ? 1 : 0);
+      auto copy_issue = [&](auto ic) {
+        constexpr int I = decltype(ic)::value;
+        if constexpr (I < KCopy::kInsts)
+          kc.template issue<I>(kvo);
+        else if constexpr (I < KCopy::kInsts + VCopy::kInsts)
+          vc.template issue<I - KCopy::kInsts>(vvo);
+        else
+          scp.issue(svo);
+      };
 
       // ---- P(j) from S(j), interleaved with S(j+1) = K(j+1) · Q^T, one 32-key half at a
       // time: the half of S(j) being turned into P is copied out of the accumulators
       // before the MFMAs of S(j+1) overwrite them ----
       bf16x8 ph[QB][2], pl[QB][2];
-      bool over = false;
       const uint32_t kn = lds_addr(knext);
       auto half = [&](auto hc) {
         constexpr int H = decltype(hc)::value;
         float sc[QB][8], scale[QB];
-        half_scores(skring + (j % 3) * kKt, kbase, H, sc, scale);
+        half_scores(mask_c, sk_addr + (j % 3) * kSkTile, kbase, H, sc, scale);
 #pragma unroll
         for (int b = 0; b < QB; ++b) sacc[b][2 * H] = sacc[b][2 * H + 1] = Acc{0, 0, 0, 0};
         // P for query block b after K step ((b + 1) * steps) / QB - 1 of this half
-        auto softmax_part = [&](int st) {
+        auto softmax_part = [&](auto st_c) {
+          constexpr int st = decltype(st_c)::value;
+          if constexpr (H == 0)
+            static_for<(st * kCopies) / Q::kSteps, ((st + 1) * kCopies) / Q::kSteps>(copy_issue);
 #pragma unroll
           for (int b = 0; b < QB; ++b) {
             if (st == ((b + 1) * Q::kSteps) / QB - 1) {
@@ -666,26 +747,30 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
 
       // Flags are double-buffered by tile parity: the write for tile j + 2 happens only
       // after every wave has passed barrier j + 1, i.e. after it read tile j's slot, so
-      // all waves read the same value and leave the loop on the same tile. A set flag
-      // stays set (it only ever leads to the restart).
+      // all waves read the same value and leave the loop on the same tile. A wave's
+      // condition never clears once raised (the running sums only grow), so rewriting
+      // the flag every tile keeps it raised.
       if (pass == 0) {
+        bool over = false;
 #pragma unroll
         for (int b = 0; b < QB; ++b) over = over || !(lacc[b][0] <= kOverSum);
-        if (__builtin_amdgcn_ballot_w64(over) != 0) flags[4 * (j & 1) + w] = 1;
+        flags[4 * (j & 1) + w] = __builtin_amdgcn_ballot_w64(over) != 0;
       }
       wait_vm_all();
       __syncthreads();   // K(j+2), V(j+1) landed; everyone is done with K(j+1) and V(j)
       if (pass == 0) {
         // act on the flags of the tile before (one tile late, so the read is off the
         // critical path; the extra tile's garbage is discarded by the restart)
-        if (flag_seen != 0) {
-          restart = true;
-          break;
-        }
+        if (flag_seen != 0) return true;
         const i32x4 f = *reinterpret_cast<const i32x4*>(flags + 4 * (j & 1));
         flag_seen = f[0] | f[1] | f[2] | f[3];
       }
-    }
+      return false;
+    };
+    bool restart = false;
+    int j = 0;
+    for (; j < n_plain && !restart; ++j) restart = body(j, std::false_type{});
+    for (; j < ntiles && !restart; ++j) restart = body(j, std::true_type{});
     if (pass == 0 && !restart && flag_seen != 0) restart = true;   // raised on the last tile
     return restart;
   };
@@ -695,12 +780,12 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
 #pragma unroll
     for (int b = 0; b < QB; ++b) m[b] = -__builtin_inff();
     for (int t = 0; t < ntiles; ++t) {
-      copy_k<PAGED, INT8K>(p, g, t * kKt, w, lane, smem, skring);
+      copy_k_all(t * kKt, 0, 0);
       wait_vm_all();
       __syncthreads();
       qk_tile(smem_addr);
       float mx[QB];
-      tile_max(skring, t * kKt, mx);
+      tile_max(sk_addr, t * kKt, mx);
 #pragma unroll
       for (int b = 0; b < QB; ++b) m[b] = fmaxf(m[b], mx[b]);
       __syncthreads();
