@@ -21,6 +21,11 @@ LIB = os.path.join(PKG, "libgqa_prefill.so")
 PROBE_LIB = os.path.join(PKG, "libgqa_layout_probe.so")
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in any generated code.
+# -amdgpu-mfma-vgpr-form: MFMA accumulators in architectural VGPRs where they fit. The
+#   attention kernel's softmax reads every score accumulator with vector ALU
+#   instructions, which cannot address AGPRs; in the AGPR form the compiler moves
+#   each one (and, short of AGPRs, part of the output accumulator) between the two
+#   files on every tile.
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
@@ -28,6 +33,7 @@ HIPCC_FLAGS = [
     "-fPIC",
     "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 
