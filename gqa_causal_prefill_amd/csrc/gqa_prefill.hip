@@ -18,23 +18,28 @@
 //     program covers tokens x heads of one GQA group, and the reuse of each K/V
 //     tile grows with the rows per program). Each wave owns QB 16-column blocks
 //     of the 16x16 MFMA output: block b = one query head, column c = one token
-//     of a 16-token run. QB = 3: a workgroup is 32 tokens x all 6 heads of g
-//     (192 rows); QB = 2: 64 tokens x a pair of g's heads (128 rows);
+//     of a 16-token run. QB = 3 (the default): a workgroup is 32 tokens x all 6
+//     heads of g (192 rows); QB = 2: 64 tokens x a pair of g's heads (128 rows);
 //   * scores are computed transposed (S^T = K·Q^T) so every lane holds keys of
-//     ONE query column: the row maxima need two permlane swaps, and the lane's
-//     S^T registers are directly the P^T operand of the P·V MFMA;
-//   * KV tiles of 64 keys arrive by global_load_lds_dwordx4 (no staging
-//     registers), double-buffered, stored chunk-major ([16-byte chunk][key]) so
-//     that K fragments are one conflict-free ds_read_b128 and the V^T operand of
-//     P·V is two ds_read_b64_tr_b16 transposing reads, all at immediate offsets;
-//   * online softmax in the exp2 domain with a lazy rescale: the running max
-//     used for the exponentials only moves when a tile raises it by more than
-//     2^8, which keeps every exponent <= 2^8 and skips almost every rescale of
-//     the accumulator registers (the result is the same softmax);
-//   * P is rounded to bf16 for the MFMA and the row sums use the rounded values.
-//     Workgroups whose first query sees fewer than 256 keys (short histories,
-//     where few keys carry large weights) multiply with P split into a bf16
-//     high part and a bf16 low part, keeping ~16 bits of P;
+//     ONE query column, and the lane's S^T registers are directly the P^T operand
+//     of the P·V MFMA;
+//   * KV tiles of 64 keys arrive by buffer loads that write LDS directly (no
+//     staging registers), double-buffered, issued a few per MFMA step over the
+//     whole iteration; rows are stored in 128-byte segments with an XOR swizzle so
+//     that K fragments are conflict-free ds_read_b128 and the V^T operand of P·V
+//     is two conflict-free ds_read_b64_tr_b16 transposing reads;
+//   * software pipeline: iteration j turns S(j) into P(j) while the MFMAs of
+//     S(j+1) run, then accumulates O += V(j)·P(j); one barrier per tile;
+//   * softmax in the exp2 domain against a fixed reference maximum per column
+//     (tile 0's maximum), so no accumulator is ever rescaled; if a column's
+//     running sum of exponentials passes 2^32 the workgroup restarts with the
+//     exact column maxima (the result is the same softmax);
+//   * P is rounded to bf16 for the MFMA and the row sums (an MFMA against ones)
+//     use the rounded values. Workgroups whose first query sees fewer than 256
+//     keys (short histories, where few keys carry large weights) multiply with P
+//     split into a bf16 high part and a bf16 low part, keeping ~16 bits of P;
+//   * the output accumulator lives in the accumulation registers (AGPRs), scores,
+//     P and fragments in the architectural VGPRs;
 //   * with INT8 keys each query row is quantised in the prologue (once per row,
 //     [INT8 QK §4]) and Q·K^T runs on v_mfma_i32_16x16x64_i8; the int32 score is
 //     scaled by sK·sQ·log2(e)/16 per score before the softmax ([INT8 QK §1]).
@@ -48,7 +53,7 @@
 #include "gqa_prefill.h"
 
 #ifndef GQA_DEFAULT_QB
-#define GQA_DEFAULT_QB 2
+#define GQA_DEFAULT_QB 3
 #endif
 
 namespace {
@@ -366,7 +371,7 @@ __device__ __forceinline__ bf16x8 vt_value(const VtFrag& f) {
 // V^T fragment (ks, db) sits at vbase[db & 3] + (db >> 2) * kSegStride + ks * 4096.
 // Fragments travel in a ring of kVtDepth + 1: step N issues the reads of step
 // N + kVtDepth, then waits for its own (2 reads per step).
-constexpr int kVtDepth = 3;
+constexpr int kVtDepth = 6;   // at most 2 (kVtDepth + 1) = 14 reads in flight: lgkmcnt counts to 15
 
 template <int N>
 __device__ __forceinline__ void vt_issue_step(VtFrag& f, const uint32_t (&vbase)[4]) {
@@ -374,22 +379,61 @@ __device__ __forceinline__ void vt_issue_step(VtFrag& f, const uint32_t (&vbase)
   vt_issue<(db >> 2) * kSegStride + ks * 4096>(f, vbase[db & 3]);
 }
 
+// O^T += V^T · P^T with the accumulator pinned to the accumulation registers (AGPRs).
+// Written as inline assembly so that the compiler keeps all output blocks there and
+// leaves the architectural VGPRs to scores, P and fragments. The compiler does not see
+// into the assembly, so the hazards it would otherwise cover are covered here:
+//  * an MFMA may read a VGPR only 2 wait states after a vector ALU instruction wrote
+//    it: FIRST marks a tile's first MFMA on each P register (P is written by the
+//    vector ALU), and the assembly then starts with s_nop 1;
+//  * V^T fragments come from LDS reads whose wait precedes the call;
+//  * consecutive MFMAs on the same accumulator need no wait states;
+//  * vector ALU accesses to the accumulators (zeroing, the epilogue) are separated
+//    from the MFMAs by agpr_fence below.
+template <bool FIRST>
+__device__ __forceinline__ void mfma_pv(f32x4& acc, const bf16x8& v, const bf16x8& p) {
+  if constexpr (FIRST)
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
+  else
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
+}
+
+// Orders every access to the output accumulators: each block is tied to a volatile
+// assembly statement (these keep their program order), and the first statement carries
+// NOPS wait states. Before the accumulators are zeroed or read by the vector ALU after
+// MFMAs, 24 wait states cover the longest MFMA-write to vector-access distance of the
+// 16x16x32 MFMAs; after zeroing, 2 cover the vector-write to MFMA-read distance.
+template <int NOPS, int QB>
+__device__ __forceinline__ void agpr_fence(f32x4 (&o)[16][QB]) {
+  static_assert(NOPS == 2 || NOPS == 24, "wait states");
+  if constexpr (NOPS == 2)
+    asm volatile("s_nop 1" : "+a"(o[0][0]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[0][0]));
+#pragma unroll
+  for (int db = 0; db < 16; ++db)
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+      if (db != 0 || b != 0) asm volatile("" : "+a"(o[db][b]));
+}
+
 template <int N, int QB, bool SPLIT>
 struct PvStep {
+  template <class Extra>
   static __device__ __forceinline__ void run(VtFrag (&vf)[kVtDepth + 1], const uint32_t (&vbase)[4],
                                              const bf16x8 (&ph)[QB][2], const bf16x8 (&pl)[QB][2],
                                              const bf16x8& ones, f32x4 (&o)[16][QB],
-                                             f32x4 (&lacc)[QB]) {
+                                             f32x4 (&lacc)[QB], Extra&& extra) {
     constexpr int ks = N >> 4, db = N & 15;
+    extra(std::integral_constant<int, N>{});
     constexpr int kAhead = (32 - 1 - N) < kVtDepth ? (32 - 1 - N) : kVtDepth;  // steps in flight after N
     if constexpr (N + kVtDepth < 32) vt_issue_step<N + kVtDepth>(vf[(N + kVtDepth) % (kVtDepth + 1)], vbase);
     vt_wait<2 * kAhead>(vf[N % (kVtDepth + 1)]);
     const bf16x8 v = vt_value(vf[N % (kVtDepth + 1)]);
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
-      o[db][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, ph[b][ks], o[db][b], 0, 0, 0);
-      if constexpr (SPLIT)
-        o[db][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pl[b][ks], o[db][b], 0, 0, 0);
+      mfma_pv<db == 0>(o[db][b], v, ph[b][ks]);
+      if constexpr (SPLIT) mfma_pv<db == 0>(o[db][b], v, pl[b][ks]);
     }
     if constexpr (db == 0) {
       // row sums from the same bf16 P the P·V product uses
@@ -400,7 +444,7 @@ struct PvStep {
           lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl[b][ks], lacc[b], 0, 0, 0);
       }
     }
-    if constexpr (N + 1 < 32) PvStep<N + 1, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc);
+    if constexpr (N + 1 < 32) PvStep<N + 1, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc, extra);
   }
 };
 
@@ -656,12 +700,14 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       copy_v_all(0, 0);
       if (ntiles > 1) copy_k_all(kKt, 1, 1);
     }
+    if constexpr (pass > 0) agpr_fence<24>(o);   // after the MFMAs of pass 0
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
 #pragma unroll
       for (int db = 0; db < 16; ++db) o[db][b] = f32x4{0.f, 0.f, 0.f, 0.f};
       lacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    agpr_fence<2>(o);
     if (pass == 0 && tid < 8) flags[tid] = 0;
     wait_vm_all();
     __syncthreads();
@@ -680,8 +726,10 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       const int kbase = j * kKt;
       const uint8_t* knext = smem + ((j + 1) & 1) * kKTile;             // K(j+1) (stale on the last tile)
       const uint8_t* vcur = smem + kVOff + (j & 1) * 4 * kSegStride;   // V(j)
-      // copies of K(j+2) and V(j+1), spread over the K steps of the first half so their
-      // issue hides under the MFMAs
+      // copies of K(j+2) and V(j+1), spread evenly over the K steps of both halves and
+      // the first 24 P·V steps: the vector memory path moves about 64 B per clock per
+      // CU, so the 64 KiB of a tile need a good part of the iteration, and issuing them
+      // in a burst would stall the waves on a full address queue
       const KCopy kc = kcopy(kbase + 2 * kKt, j & 1);
       const VCopy vc = vcopy(kbase + kKt, (j + 1) & 1);
       ScaleCopy scp;
@@ -695,6 +743,15 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
           vc.template issue<I - KCopy::kInsts>(vvo);
         else
           scp.issue(svo);
+      };
+      constexpr int kSlots = 2 * Q::kSteps + 24;   // issue slots: K steps, then P·V steps
+      // the copies whose slot (I * kSlots) / kCopies is SLOT
+      auto copies_at = [&](auto slot_c) {
+        constexpr int kSlot = decltype(slot_c)::value;
+        static_for<0, kCopies>([&](auto ic) {
+          constexpr int I = decltype(ic)::value;
+          if constexpr ((I * kSlots) / kCopies == kSlot) copy_issue(ic);
+        });
       };
 
       // ---- P(j) from S(j), interleaved with S(j+1) = K(j+1) · Q^T, one 32-key half at a
@@ -711,8 +768,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
         // P for query block b after K step ((b + 1) * steps) / QB - 1 of this half
         auto softmax_part = [&](auto st_c) {
           constexpr int st = decltype(st_c)::value;
-          if constexpr (H == 0)
-            static_for<(st * kCopies) / Q::kSteps, ((st + 1) * kCopies) / Q::kSteps>(copy_issue);
+          copies_at(std::integral_constant<int, H * Q::kSteps + st>{});
 #pragma unroll
           for (int b = 0; b < QB; ++b) {
             if (st == ((b + 1) * Q::kSteps) / QB - 1) {
@@ -739,10 +795,12 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) vbase[jj] = v0 + vbase_off[jj];
         VtFrag vf[kVtDepth + 1];
-        vt_issue_step<0>(vf[0], vbase);
-        vt_issue_step<1>(vf[1], vbase);
-        vt_issue_step<2>(vf[2], vbase);
-        PvStep<0, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc);
+        static_for<0, kVtDepth>([&](auto nc) {   // the first kVtDepth steps' reads
+          vt_issue_step<decltype(nc)::value>(vf[decltype(nc)::value], vbase);
+        });
+        PvStep<0, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc, [&](auto nc) {
+          copies_at(std::integral_constant<int, 2 * Q::kSteps + decltype(nc)::value>{});
+        });
       }
 
       // Flags are double-buffered by tile parity: the write for tile j + 2 happens only
@@ -794,6 +852,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   }
 
   // ---- epilogue: O / l -> bf16 ----
+  agpr_fence<24>(o);
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const float inv = 1.0f / lacc[b][0];

@@ -113,11 +113,12 @@ def test_quantizer_argument_checks():
 def test_plan_describes_the_dispatch():
     plan = binding.gqa_attn_prefill_plan(4096, 32768)
     assert "variant=bf16_contiguous" in plan
-    # one workgroup per (KV head, head pair, 64-token block): 4 * 3 * 64
-    assert "workgroups=768" in plan and "threads=256" in plan
+    # one workgroup per (KV head, 32-token block) covering the 6 query heads of the
+    # group: 4 * 128
+    assert "workgroups=512" in plan and "threads=256" in plan
     assert "variant=bf16_paged" in binding.gqa_attn_prefill_plan(512, 32768, paged=True)
     assert "variant=int8k" in binding.gqa_attn_prefill_plan(3072, 16384, int8k=True)
-    assert "workgroups=12" in binding.gqa_attn_prefill_plan(1, 1)
+    assert "workgroups=4" in binding.gqa_attn_prefill_plan(1, 1)
     with pytest.raises(binding.GqaError):
         binding.gqa_attn_prefill_plan(512, 32768, paged=True, int8k=True)
     with pytest.raises(binding.GqaError):
