@@ -1,7 +1,8 @@
 """Benchmark of causal GQA prefill attention on one MI355X.
 
-A step is one gqa_attn_prefill call (the whole hot path: Q load/quantise, K/V
-tile fetch, Q·K^T, scale and causal mask, online softmax, P·V, epilogue) over
+A step is one gqa_attn_prefill_ws call (the whole hot path: Q load/quantise, K/V
+tile fetch, Q·K^T, scale and causal mask, softmax, P·V, epilogue, and the merge of
+KV segments when the call splits the history) over
 the q_len 4096 x kv_len 32768 chunk (24 query heads, 4 KV heads, head_dim 256,
 bf16, contiguous KV) unless --workload says otherwise. Inputs are seeded
 synthetic tensors already resident in HBM when the timed region starts.
@@ -120,9 +121,12 @@ def main():
         k = d["k"].to(dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
+    # KV-segment workspace (empty when the call runs unsplit), allocated before timing
+    ws_bytes = gqa.gqa_attn_prefill_workspace_size(w.q_len, w.kv_len, w.paged, w.int8k)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     def step():
-        gqa.gqa_attn_prefill(q, k, v, out=out, stream=stream, **kw)
+        gqa.gqa_attn_prefill_ws(q, k, v, out=out, workspace=ws, stream=stream, **kw)
 
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20)

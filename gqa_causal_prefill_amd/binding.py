@@ -29,6 +29,7 @@ _STATUS_NAMES = {
     3: "GQA_ERR_MISALIGNED",
     4: "GQA_ERR_UNSUPPORTED",
     5: "GQA_ERR_HIP",
+    6: "GQA_ERR_WORKSPACE",
 }
 
 
@@ -59,6 +60,11 @@ def library() -> ctypes.CDLL:
         lib.gqa_status_string.argtypes = [ctypes.c_int]
         lib.gqa_attn_prefill.restype = ctypes.c_int
         lib.gqa_attn_prefill.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, vp]
+        lib.gqa_attn_prefill_ws.restype = ctypes.c_int
+        lib.gqa_attn_prefill_ws.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, vp,
+                                            ctypes.c_size_t, vp]
+        lib.gqa_attn_prefill_workspace_size.restype = ctypes.c_size_t
+        lib.gqa_attn_prefill_workspace_size.argtypes = [i32, i32, ctypes.c_int, ctypes.c_int]
         lib.gqa_quantize_rows_int8.restype = ctypes.c_int
         lib.gqa_quantize_rows_int8.argtypes = [vp, i64, vp, vp, vp]
         lib.gqa_attn_prefill_plan.restype = ctypes.c_int
@@ -84,6 +90,12 @@ def gqa_attn_prefill_plan(q_len: int, kv_len: int, paged: bool = False, int8k: b
     return buf.value.decode()
 
 
+def gqa_attn_prefill_workspace_size(q_len: int, kv_len: int, paged: bool = False,
+                                    int8k: bool = False) -> int:
+    """Bytes of workspace gqa_attn_prefill_ws needs (0: it runs unsplit)."""
+    return int(library().gqa_attn_prefill_workspace_size(q_len, kv_len, int(paged), int(int8k)))
+
+
 def _stream_handle(t: torch.Tensor, stream):
     if stream is None:
         stream = torch.cuda.current_stream(t.device)
@@ -105,18 +117,8 @@ def _expect(t, name, dtype, shape, device):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def gqa_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                     block_table: torch.Tensor | None = None, num_blocks: int | None = None,
-                     k_scale: torch.Tensor | None = None, q_len: int | None = None,
-                     kv_len: int | None = None, out: torch.Tensor | None = None,
-                     stream=None) -> torch.Tensor:
-    """Causal GQA prefill attention; see gqa_attn_prefill in include/gqa_prefill.h.
-
-    q: bf16 [q_len, 24, 256]. Contiguous: k, v [kv_len, 4, 256]. Paged (block_table
-    given): k, v caches [num_blocks, 4, 16, 256] and block_table int32
-    [ceil(kv_len / 16)] (kv_len must then be given). INT8 keys: k int8 and
-    k_scale float32 [kv_len, 4]. Returns out (bf16 [q_len, 24, 256]).
-    """
+def _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out):
+    """Checks dtypes, shapes, contiguity and device; returns the C arguments and out."""
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("gqa_attn_prefill runs on the GPU; q is on " + str(dev))
@@ -142,11 +144,53 @@ def gqa_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         out = torch.empty((q_len, NUM_Q_HEADS, HEAD_DIM), dtype=torch.bfloat16, device=dev)
     else:
         _expect(out, "out", torch.bfloat16, (q_len, NUM_Q_HEADS, HEAD_DIM), dev)
-    st = library().gqa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(block_table), nb,
-                                    _ptr(k_scale), q_len, kv_len, _ptr(out),
-                                    _stream_handle(q, stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(block_table), nb, _ptr(k_scale), q_len, kv_len,
+            _ptr(out))
+    return args, out, (q_len, kv_len, paged, k_scale is not None)
+
+
+def gqa_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     block_table: torch.Tensor | None = None, num_blocks: int | None = None,
+                     k_scale: torch.Tensor | None = None, q_len: int | None = None,
+                     kv_len: int | None = None, out: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """Causal GQA prefill attention; see gqa_attn_prefill in include/gqa_prefill.h.
+
+    q: bf16 [q_len, 24, 256]. Contiguous: k, v [kv_len, 4, 256]. Paged (block_table
+    given): k, v caches [num_blocks, 4, 16, 256] and block_table int32
+    [ceil(kv_len / 16)] (kv_len must then be given). INT8 keys: k int8 and
+    k_scale float32 [kv_len, 4]. Returns out (bf16 [q_len, 24, 256]).
+    """
+    args, out, _ = _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out)
+    st = library().gqa_attn_prefill(*args, _stream_handle(q, stream))
     if st != GQA_OK:
         raise GqaError(st, "gqa_attn_prefill")
+    return out
+
+
+def gqa_attn_prefill_ws(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        block_table: torch.Tensor | None = None, num_blocks: int | None = None,
+                        k_scale: torch.Tensor | None = None, q_len: int | None = None,
+                        kv_len: int | None = None, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """gqa_attn_prefill that may split the history into KV segments (see
+    gqa_attn_prefill_ws in include/gqa_prefill.h). `workspace` is a device tensor of
+    at least gqa_attn_prefill_workspace_size() bytes; when it is None and the call
+    splits, one is allocated through torch for this call."""
+    args, out, (ql, kl, paged, int8k) = _prefill_args(q, k, v, block_table, num_blocks,
+                                                      k_scale, q_len, kv_len, out)
+    need = gqa_attn_prefill_workspace_size(ql, kl, paged, int8k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        if workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on " + str(q.device))
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    else:
+        ws_ptr, ws_bytes = None, 0
+    st = library().gqa_attn_prefill_ws(*args, ws_ptr, ws_bytes, _stream_handle(q, stream))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_attn_prefill_ws")
     return out
 
 

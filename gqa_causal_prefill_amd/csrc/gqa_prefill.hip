@@ -48,6 +48,7 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "gqa_prefill.h"
@@ -98,6 +99,9 @@ struct Params {
   int32_t q_len;
   int32_t kv_len;
   int32_t n_tblk;          // token blocks of the grid
+  int32_t n_seg;           // KV segments per (KV head, token block); 1 = the whole history
+  float* ws_o;             // n_seg > 1: unnormalised O [n_seg, q_len, 24, 256]
+  float* ws_ml;            // n_seg > 1: (reference maximum, row sum) [n_seg, q_len, 24, 2]
 };
 
 // Workgroup shape for QB 16-column query blocks per wave.
@@ -484,12 +488,13 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   const int tw = w % S::kTokenBlocks;
   const int hw = w / S::kTokenBlocks;
 
-  // Workgroup id -> (KV head, head subset, token block). id % 4 is the KV head, so
-  // workgroups dispatched round-robin over the 8 XCDs keep one KV head per XCD (its
-  // K/V stream shares that XCD's L2); token blocks go longest first.
+  // Workgroup id -> (KV head, KV segment, head subset, token block). id % 4 is the KV
+  // head, so workgroups dispatched round-robin over the 8 XCDs keep one KV head per
+  // XCD (its K/V stream shares that XCD's L2); token blocks go longest first.
   const int id = blockIdx.x;
   const int g = id & (kHkv - 1);
-  const int rest = id >> 2;
+  const int seg = (id >> 2) % p.n_seg;
+  const int rest = (id >> 2) / p.n_seg;
   const int hsel = rest % S::kSplitsPerGroup;
   const int tblk = p.n_tblk - 1 - rest / S::kSplitsPerGroup;
   const int t0 = tblk * S::kTokPerWg;
@@ -502,7 +507,22 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   const int limit = off + tok;   // last visible key of this column
 
   const int last_tok = min(t0 + S::kTokPerWg, p.q_len);
-  const int ntiles = (off + last_tok + kKt - 1) / kKt;
+  const int ntiles = (off + last_tok + kKt - 1) / kKt;   // tiles of the whole history
+  // This workgroup's KV segment: tiles [j0, j1). The host makes every segment at least
+  // 8 tiles long, so each segment starts at or before the workgroup's first query and
+  // its first key is visible to every query of the workgroup (the pass-0 reference
+  // below is then a real score of every column).
+  const int j0 = (int)(((int64_t)ntiles * seg) / p.n_seg);
+  const int j1 = (int)(((int64_t)ntiles * (seg + 1)) / p.n_seg);
+  if (j0 >= j1) {   // empty segment (not produced by the host's plans): weight 0 in the merge
+    if (tok_ok && L == 0) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+        *reinterpret_cast<float2*>(p.ws_ml + (((size_t)seg * p.q_len + tok) * kHq + head0 + b) * 2) =
+            make_float2(-__builtin_inff(), 0.0f);
+    }
+    return;
+  }
 
   // ---- tile copies (this wave's 16 keys of each tile) ----
   using KCopy = WaveCopy<PAGED, INT8K ? kD : 2 * kD, false>;
@@ -533,9 +553,9 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   };
 
   // start the first copies before the Q prologue
-  copy_k_all(0, 0, 0);
-  copy_v_all(0, 0);
-  if (ntiles > 1) copy_k_all(kKt, 1, 1);
+  copy_k_all(j0 * kKt, j0 & 1, j0 % 3);
+  copy_v_all(j0 * kKt, j0 & 1);
+  if (j1 - j0 > 1) copy_k_all((j0 + 1) * kKt, (j0 + 1) & 1, (j0 + 1) % 3);
 
   // ---- prologue: Q fragments (B operand of S^T = K·Q^T) ----
   typename Q::Frag qf[QB][Q::kSteps];
@@ -696,9 +716,9 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   auto main_pass = [&](auto pass_c) -> bool {
     constexpr int pass = decltype(pass_c)::value;
     if constexpr (pass > 0) {
-      copy_k_all(0, 0, 0);
-      copy_v_all(0, 0);
-      if (ntiles > 1) copy_k_all(kKt, 1, 1);
+      copy_k_all(j0 * kKt, j0 & 1, j0 % 3);
+      copy_v_all(j0 * kKt, j0 & 1);
+      if (j1 - j0 > 1) copy_k_all((j0 + 1) * kKt, (j0 + 1) & 1, (j0 + 1) % 3);
     }
     if constexpr (pass > 0) agpr_fence<24>(o);   // after the MFMAs of pass 0
 #pragma unroll
@@ -711,15 +731,15 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     if (pass == 0 && tid < 8) flags[tid] = 0;
     wait_vm_all();
     __syncthreads();
-    qk_tile(smem_addr);   // S(0)
-    if (pass == 0) tile_max(sk_addr, 0, m);
-    __syncthreads();   // every wave is done with K(0) before K(2) overwrites it
+    qk_tile(smem_addr + (j0 & 1) * kKTile);   // S(j0)
+    if (pass == 0) tile_max(sk_addr + (j0 % 3) * kSkTile, j0 * kKt, m);
+    __syncthreads();   // every wave is done with K(j0) before K(j0+2) overwrites it
 
     // Tiles that end at or before the workgroup's first query need no causal mask; the
     // rest (one or two per workgroup) run the masked form of the same body. The body
     // is one basic block: copies past the last tile re-read the clamped last key into a
     // buffer nothing reads again, and the restart flag is rewritten every tile.
-    const int n_plain = min(ntiles, (off + t0 + 1) / kKt);
+    const int n_plain = min(j1, (off + t0 + 1) / kKt);
     int flag_seen = 0;   // flags read after the previous tile's barrier
     // returns true when pass 0 must restart
     auto body = [&](int j, auto mask_c) -> bool {
@@ -730,10 +750,13 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       // the first 24 P·V steps: the vector memory path moves about 64 B per clock per
       // CU, so the 64 KiB of a tile need a good part of the iteration, and issuing them
       // in a burst would stall the waves on a full address queue
-      const KCopy kc = kcopy(kbase + 2 * kKt, j & 1);
-      const VCopy vc = vcopy(kbase + kKt, (j + 1) & 1);
+      // (a tile past the segment is fetched from kv_len on: no rows, no traffic)
+      const int kb2 = j + 2 < j1 ? kbase + 2 * kKt : p.kv_len;
+      const int kb1 = j + 1 < j1 ? kbase + kKt : p.kv_len;
+      const KCopy kc = kcopy(kb2, j & 1);
+      const VCopy vc = vcopy(kb1, (j + 1) & 1);
       ScaleCopy scp;
-      if constexpr (INT8K) scp = scopy(kbase + 2 * kKt, (j + 2) % 3);
+      if constexpr (INT8K) scp = scopy(kb2, (j + 2) % 3);
       constexpr int kCopies = KCopy::kInsts + VCopy::kInsts + (INT8K ? 1 : 0);
       auto copy_issue = [&](auto ic) {
         constexpr int I = decltype(ic)::value;
@@ -826,9 +849,9 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       return false;
     };
     bool restart = false;
-    int j = 0;
+    int j = j0;
     for (; j < n_plain && !restart; ++j) restart = body(j, std::false_type{});
-    for (; j < ntiles && !restart; ++j) restart = body(j, std::true_type{});
+    for (; j < j1 && !restart; ++j) restart = body(j, std::true_type{});
     if (pass == 0 && !restart && flag_seen != 0) restart = true;   // raised on the last tile
     return restart;
   };
@@ -837,7 +860,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     // ---- exact column maxima over every visible key (max-only sweep), then pass 1 ----
 #pragma unroll
     for (int b = 0; b < QB; ++b) m[b] = -__builtin_inff();
-    for (int t = 0; t < ntiles; ++t) {
+    for (int t = j0; t < j1; ++t) {
       copy_k_all(t * kKt, 0, 0);
       wait_vm_all();
       __syncthreads();
@@ -851,8 +874,23 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     main_pass(std::integral_constant<int, 1>{});
   }
 
-  // ---- epilogue: O / l -> bf16 ----
   agpr_fence<24>(o);
+  if (p.n_seg > 1) {
+    // ---- epilogue of one KV segment: unnormalised O, the reference maximum (log2
+    // units, scale included) and the row sum, merged by merge_segments_kernel ----
+    if (tok_ok) {
+      const size_t row0 = ((size_t)seg * p.q_len + tok) * kHq + head0;
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        float* orow = p.ws_o + (row0 + b) * kD;
+#pragma unroll
+        for (int db = 0; db < 16; ++db) *reinterpret_cast<f32x4*>(orow + 16 * db + 4 * L) = o[db][b];
+        if (L == 0) *reinterpret_cast<float2*>(p.ws_ml + (row0 + b) * 2) = make_float2(m[b], lacc[b][0]);
+      }
+    }
+    return;
+  }
+  // ---- epilogue: O / l -> bf16 ----
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const float inv = 1.0f / lacc[b][0];
@@ -872,12 +910,44 @@ template <bool PAGED, bool INT8K, int QB>
 __global__ __launch_bounds__(kThreads, 1) void gqa_prefill_kernel(const Params p) {
   using S = Shape<QB>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[lds_bytes<PAGED, INT8K, QB>()];
-  const int rest = blockIdx.x >> 2;
+  const int rest = (blockIdx.x >> 2) / p.n_seg;
   const int t0 = (p.n_tblk - 1 - rest / S::kSplitsPerGroup) * S::kTokPerWg;
   if (p.kv_len - p.q_len + t0 + 1 < kSplitBelow)
     run<PAGED, INT8K, QB, true>(p, smem);
   else
     run<PAGED, INT8K, QB, false>(p, smem);
+}
+
+// ---- merge of KV segments: one wave per output row (token, head), 4 features a lane ----
+// Each segment took its exponentials against its own reference maximum m_s (log2
+// units) and left unnormalised O_s and the row sum l_s. With M the largest m_s,
+//   out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
+// the softmax over the whole history (a segment with l_s = 0 has no keys and weight 0).
+// Long histories are cut into segments the same way for decode attention and for
+// chunked prefill on the pages ("gfx936 DCU上实现INT8 QK MMAC" §4).
+__global__ __launch_bounds__(256) void merge_segments_kernel(const float* ws_o, const float* ws_ml,
+                                                             int n_seg, int64_t rows, uint8_t* out) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml);
+  float mmax = -__builtin_inff();
+  for (int sg = 0; sg < n_seg; ++sg) {
+    const float2 v = ml[sg * rows + row];
+    if (v.y > 0.0f) mmax = fmaxf(mmax, v.x);
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.0f;
+  for (int sg = 0; sg < n_seg; ++sg) {
+    const float2 v = ml[sg * rows + row];
+    if (v.y > 0.0f) {
+      const float wgt = __builtin_amdgcn_exp2f(v.x - mmax);
+      lsum += wgt * v.y;
+      acc += wgt * *reinterpret_cast<const f32x4*>(ws_o + ((size_t)(sg * rows + row)) * kD + 4 * lane);
+    }
+  }
+  const f32x4 y = acc * (1.0f / lsum);
+  *reinterpret_cast<bf16x4*>(out + ((size_t)row * kD + 4 * lane) * 2) = __builtin_convertvector(y, bf16x4);
 }
 
 // ---- standalone row quantiser: one wave per 256-element row ----
@@ -942,6 +1012,28 @@ Launch shape_launch(int32_t q_len, bool int8k) {
   return lc;
 }
 
+constexpr int kCUs = 256;        // compute units of an MI355X
+constexpr int kMinSegTiles = 8;  // shortest KV segment (512 keys)
+
+// KV segments per (KV head, token block) for a call that has a workspace: 1 while the
+// unsplit grid already gives every CU a workgroup, else enough segments for about two
+// workgroups per CU, each at least kMinSegTiles tiles long in the shortest (first) token
+// block. INT8 keys are not split: each segment would quantise its query rows again,
+// which the pages keep to once per row ("gfx936 DCU上实现INT8 QK MMAC" §4).
+int segments_for(int32_t q_len, int32_t kv_len, bool int8k, int unsplit_workgroups) {
+  if (int8k || unsplit_workgroups >= kCUs || q_len == 0) return 1;
+  const int first_tok_block = std::min<int32_t>(q_len, Shape<GQA_DEFAULT_QB>::kTokPerWg);
+  const int64_t t_min = ((int64_t)kv_len - q_len + first_tok_block + kKt - 1) / kKt;
+  int n = (2 * kCUs + unsplit_workgroups - 1) / unsplit_workgroups;
+  n = (int)std::min<int64_t>(n, t_min / kMinSegTiles);
+  return std::max(n, 1);
+}
+
+size_t workspace_bytes_for(int32_t q_len, int n_seg) {
+  if (n_seg <= 1) return 0;
+  return (size_t)n_seg * q_len * kHq * (kD + 2) * sizeof(float);
+}
+
 // Dispatch rule (the analogue of the pages' q_len/kv_len-gated variant choice): one
 // kernel family; the query-block count per wave is the only shape parameter.
 Launch plan_for(int32_t q_len, int32_t kv_len, bool paged, bool int8k) {
@@ -954,6 +1046,66 @@ Launch plan_for(int32_t q_len, int32_t kv_len, bool paged, bool int8k) {
   else
     lc.name = kDefaultQB == 3 ? "bf16_contiguous_t32h6_kt64" : "bf16_contiguous_t64h2_kt64";
   return lc;
+}
+
+// Shared by both entry points; `allow_split` is false for the call without a workspace.
+int prefill(const void* q, const void* k, const void* v, const int32_t* block_table,
+            int32_t num_blocks, const float* k_scale, int32_t q_len, int32_t kv_len, void* out,
+            void* workspace, size_t workspace_bytes, bool allow_split, void* stream) {
+  int st = check_prefill_lengths(q_len, kv_len);
+  if (st != GQA_OK) return st;
+  if (q_len == 0) return GQA_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return GQA_ERR_NULL_ARG;
+  const bool paged = block_table != nullptr;
+  const bool int8k = k_scale != nullptr;
+  if (paged && int8k) return GQA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return GQA_ERR_MISALIGNED;
+  if (paged && !aligned(block_table, 4)) return GQA_ERR_MISALIGNED;
+  if (int8k && !aligned(k_scale, 4)) return GQA_ERR_MISALIGNED;
+  if (paged) {
+    const int64_t need = ((int64_t)kv_len + kBs - 1) / kBs;
+    if (num_blocks < need || num_blocks <= 0) return GQA_ERR_BAD_LENGTH;
+  }
+  const Launch lc = plan_for(q_len, kv_len, paged, int8k);
+  const int n_seg = allow_split ? segments_for(q_len, kv_len, int8k, lc.workgroups) : 1;
+  const size_t ws_need = workspace_bytes_for(q_len, n_seg);
+  if (n_seg > 1) {
+    if (workspace == nullptr || workspace_bytes < ws_need) return GQA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return GQA_ERR_MISALIGNED;
+  }
+
+  Params p;
+  p.q = static_cast<const uint8_t*>(q);
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v);
+  p.bt = block_table;
+  p.ks = k_scale;
+  p.out = static_cast<uint8_t*>(out);
+  p.num_blocks = paged ? num_blocks : 0;
+  p.q_len = q_len;
+  p.kv_len = kv_len;
+  p.n_tblk = lc.n_tblk;
+  p.n_seg = n_seg;
+  p.ws_o = n_seg > 1 ? static_cast<float*>(workspace) : nullptr;
+  p.ws_ml = n_seg > 1 ? p.ws_o + (size_t)n_seg * q_len * kHq * kD : nullptr;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(lc.workgroups * n_seg), block(lc.threads);
+  if (int8k)
+    hipLaunchKernelGGL((gqa_prefill_kernel<false, true, kDefaultQB>), grid, block, 0, s, p);
+  else if (paged)
+    hipLaunchKernelGGL((gqa_prefill_kernel<true, false, kDefaultQB>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((gqa_prefill_kernel<false, false, kDefaultQB>), grid, block, 0, s, p);
+  if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
+  if (n_seg > 1) {
+    const int64_t rows = (int64_t)q_len * kHq;
+    hipLaunchKernelGGL(merge_segments_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+                       p.ws_o, p.ws_ml, n_seg, rows, p.out);
+    if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
+  }
+  return GQA_OK;
 }
 
 }  // namespace
@@ -970,6 +1122,7 @@ const char* gqa_status_string(int status) {
     case GQA_ERR_MISALIGNED: return "a tensor pointer is misaligned";
     case GQA_ERR_UNSUPPORTED: return "unsupported combination (paged caches with INT8 keys)";
     case GQA_ERR_HIP: return "HIP launch failed";
+    case GQA_ERR_WORKSPACE: return "workspace missing or smaller than gqa_attn_prefill_workspace_size()";
     default: return "unknown status";
   }
 }
@@ -983,52 +1136,31 @@ int gqa_attn_prefill_plan(int32_t q_len, int32_t kv_len, int paged, int int8k, c
     return st;
   }
   const Launch lc = plan_for(q_len, kv_len, paged != 0, int8k != 0);
-  snprintf(buf, n, "variant=%s workgroups=%d threads=%d lds_bytes=%d", lc.name, lc.workgroups,
-           lc.threads, lc.lds_bytes);
+  const int n_seg = segments_for(q_len, kv_len, int8k != 0, lc.workgroups);
+  snprintf(buf, n, "variant=%s workgroups=%d threads=%d lds_bytes=%d segments=%d workspace_bytes=%zu",
+           lc.name, lc.workgroups * n_seg, lc.threads, lc.lds_bytes, n_seg,
+           workspace_bytes_for(q_len, n_seg));
   return GQA_OK;
+}
+
+size_t gqa_attn_prefill_workspace_size(int32_t q_len, int32_t kv_len, int paged, int int8k) {
+  if (check_prefill_lengths(q_len, kv_len) != GQA_OK || (paged && int8k)) return 0;
+  const Launch lc = plan_for(q_len, kv_len, paged != 0, int8k != 0);
+  return workspace_bytes_for(q_len, segments_for(q_len, kv_len, int8k != 0, lc.workgroups));
 }
 
 int gqa_attn_prefill(const void* q, const void* k, const void* v, const int32_t* block_table,
                      int32_t num_blocks, const float* k_scale, int32_t q_len, int32_t kv_len,
                      void* out, void* stream) {
-  int st = check_prefill_lengths(q_len, kv_len);
-  if (st != GQA_OK) return st;
-  if (q_len == 0) return GQA_OK;
-  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return GQA_ERR_NULL_ARG;
-  const bool paged = block_table != nullptr;
-  const bool int8k = k_scale != nullptr;
-  if (paged && int8k) return GQA_ERR_UNSUPPORTED;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
-    return GQA_ERR_MISALIGNED;
-  if (paged && !aligned(block_table, 4)) return GQA_ERR_MISALIGNED;
-  if (int8k && !aligned(k_scale, 4)) return GQA_ERR_MISALIGNED;
-  if (paged) {
-    const int64_t need = ((int64_t)kv_len + kBs - 1) / kBs;
-    if (num_blocks < need || num_blocks <= 0) return GQA_ERR_BAD_LENGTH;
-  }
+  return prefill(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out, nullptr, 0, false,
+                 stream);
+}
 
-  Params p;
-  p.q = static_cast<const uint8_t*>(q);
-  p.k = static_cast<const uint8_t*>(k);
-  p.v = static_cast<const uint8_t*>(v);
-  p.bt = block_table;
-  p.ks = k_scale;
-  p.out = static_cast<uint8_t*>(out);
-  p.num_blocks = paged ? num_blocks : 0;
-  p.q_len = q_len;
-  p.kv_len = kv_len;
-
-  const Launch lc = plan_for(q_len, kv_len, paged, int8k);
-  p.n_tblk = lc.n_tblk;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(lc.workgroups), block(lc.threads);
-  if (int8k)
-    hipLaunchKernelGGL((gqa_prefill_kernel<false, true, kDefaultQB>), grid, block, 0, s, p);
-  else if (paged)
-    hipLaunchKernelGGL((gqa_prefill_kernel<true, false, kDefaultQB>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((gqa_prefill_kernel<false, false, kDefaultQB>), grid, block, 0, s, p);
-  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+int gqa_attn_prefill_ws(const void* q, const void* k, const void* v, const int32_t* block_table,
+                        int32_t num_blocks, const float* k_scale, int32_t q_len, int32_t kv_len,
+                        void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out, workspace,
+                 workspace_bytes, true, stream);
 }
 
 int gqa_quantize_rows_int8(const void* x, int64_t rows, void* xq, float* scale, void* stream) {

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define GQA_ABI_VERSION 1
+#define GQA_ABI_VERSION 2
 #define GQA_NUM_Q_HEADS 24
 #define GQA_NUM_KV_HEADS 4
 #define GQA_HEAD_DIM 256
@@ -56,7 +56,8 @@ typedef enum gqa_status {
                                rows < 0, or num_blocks too small for kv_len */
   GQA_ERR_MISALIGNED = 3,   /* a tensor pointer is not aligned as documented */
   GQA_ERR_UNSUPPORTED = 4,  /* a combination this library refuses (paged + INT8 K) */
-  GQA_ERR_HIP = 5           /* the HIP launch failed */
+  GQA_ERR_HIP = 5,          /* the HIP launch failed */
+  GQA_ERR_WORKSPACE = 6     /* gqa_attn_prefill_ws: workspace NULL or too small */
 } gqa_status;
 
 /* Version of this interface; equals GQA_ABI_VERSION of the header the library
@@ -102,6 +103,45 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v,
                      void* out, void* stream);
 
 /*
+ * gqa_attn_prefill_workspace_size - bytes of device workspace gqa_attn_prefill_ws
+ * needs for a call with these lengths; 0 when it runs the history in one piece.
+ *
+ * Long histories may be cut into KV segments, as the pages do for decode attention
+ * and for chunked prefill with history ("gfx936 DCU上实现INT8 QK MMAC" §4): this
+ * happens when q_len is so short that one workgroup per (KV head, 32 query tokens)
+ * would leave compute units idle. Each segment then writes its unnormalised output,
+ * its per-row reference maximum and row sum to the workspace, and a merge step
+ * combines them by the log-sum-exp rule into `out`. INT8 keys are never split (each
+ * segment would quantise the query rows again).
+ *
+ * paged, int8k: 0 or 1. Pure host function. Returns 0 for arguments
+ * gqa_attn_prefill_ws would refuse.
+ */
+size_t gqa_attn_prefill_workspace_size(int32_t q_len, int32_t kv_len, int paged,
+                                       int int8k);
+
+/*
+ * gqa_attn_prefill_ws - gqa_attn_prefill with a caller-provided workspace, which
+ * lets the call split the history into KV segments (see above). Same arguments,
+ * layouts and result as gqa_attn_prefill (up to float rounding), plus:
+ *
+ * workspace        device memory, 16-byte aligned, owned by the caller; may be
+ *                  NULL when gqa_attn_prefill_workspace_size() is 0. Its
+ *                  contents on entry are ignored and on return unspecified; it
+ *                  must not overlap any other argument, and two calls in flight
+ *                  at once must not share it.
+ * workspace_bytes  its size in bytes.
+ *
+ * Returns the codes of gqa_attn_prefill and GQA_ERR_WORKSPACE when the split needs
+ * a workspace and it is NULL or smaller than gqa_attn_prefill_workspace_size().
+ */
+int gqa_attn_prefill_ws(const void* q, const void* k, const void* v,
+                        const int32_t* block_table, int32_t num_blocks,
+                        const float* k_scale, int32_t q_len, int32_t kv_len,
+                        void* out, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
  * gqa_quantize_rows_int8 - the per-row INT8 quantiser of "gfx936 DCU上实现INT8 QK
  * MMAC" §1/§4 as a standalone step (the K-cache producer's quantisation; the
  * attention call applies the same rule to Q internally).
@@ -120,9 +160,11 @@ int gqa_quantize_rows_int8(const void* x, int64_t rows, void* xq, float* scale,
                            void* stream);
 
 /*
- * gqa_attn_prefill_plan - the launch the dispatcher would choose for a call
+ * gqa_attn_prefill_plan - the launch gqa_attn_prefill_ws would choose for a call
  * with these lengths (variant name, workgroup count, threads per workgroup,
- * bytes of LDS), written as text into buf (at most n bytes, NUL-terminated).
+ * bytes of LDS, KV segments, workspace bytes), written as text into buf (at most
+ * n bytes, NUL-terminated). gqa_attn_prefill makes the same choice with one
+ * segment.
  * Pure host function: touches no device. The variant depends on the lengths
  * the same way the pages' dispatch depends on the real q_len and kv_len of a
  * chunk ("DCU使用技术报告（中篇）" §3, §5).

@@ -13,7 +13,7 @@ from gqa_causal_prefill_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER_DIR = os.path.join(ROOT, "include")
 
-OK, NULL, BADLEN, MISALIGNED, UNSUPPORTED, HIPERR = range(6)
+OK, NULL, BADLEN, MISALIGNED, UNSUPPORTED, HIPERR, WORKSPACE = range(7)
 
 
 def _have_lib():
@@ -35,8 +35,9 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"gqa_attn_prefill", "gqa_quantize_rows_int8", "gqa_attn_prefill_plan",
-            "gqa_abi_version", "gqa_status_string"} <= set(names)
+    assert {"gqa_attn_prefill", "gqa_attn_prefill_ws", "gqa_attn_prefill_workspace_size",
+            "gqa_quantize_rows_int8", "gqa_attn_prefill_plan", "gqa_abi_version",
+            "gqa_status_string"} <= set(names)
     lib = ctypes.CDLL(gqa_build.LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -51,8 +52,8 @@ def test_probe_library_loads():
 
 
 def test_abi_version_and_status_strings():
-    assert binding.gqa_abi_version() == 1
-    for s in range(6):
+    assert binding.gqa_abi_version() == 2
+    for s in range(7):
         assert binding.gqa_status_string(s)
     assert binding.gqa_status_string(99) == "unknown status"
 
@@ -132,3 +133,53 @@ def test_binding_refuses_cpu_tensors():
     k = torch.zeros(8, 4, 256, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         binding.gqa_attn_prefill(q, k, k)
+
+
+# ------------------------------------------------------------------ KV segments and workspace
+
+def ws_call(ws, ws_bytes, q_len=512, kv_len=32768, bt=None, nb=0):
+    lib = binding.library()
+    vp = ctypes.c_void_p
+    return lib.gqa_attn_prefill_ws(vp(16), vp(16), vp(16), vp(bt), nb, None, q_len, kv_len,
+                                   vp(16), vp(ws), ws_bytes, None)
+
+
+SPLIT_512x32768 = 8 * 512 * 24 * (256 + 2) * 4   # 8 segments of fp32 (O, m, l) per row
+
+
+def test_workspace_size():
+    # a grid that fills the chip runs unsplit and needs nothing
+    assert binding.gqa_attn_prefill_workspace_size(4096, 32768) == 0
+    assert binding.gqa_attn_prefill_workspace_size(3072, 16384, int8k=True) == 0
+    # 512 queries: 4 KV heads x 16 token blocks = 64 workgroups -> 8 segments of 63 tiles
+    assert binding.gqa_attn_prefill_workspace_size(512, 32768) == SPLIT_512x32768
+    assert binding.gqa_attn_prefill_workspace_size(512, 32768, paged=True) == SPLIT_512x32768
+    # INT8 keys are never split; short histories are not split below 8 tiles a segment
+    assert binding.gqa_attn_prefill_workspace_size(512, 32768, int8k=True) == 0
+    assert binding.gqa_attn_prefill_workspace_size(32, 500) == 0
+    # arguments the call would refuse
+    assert binding.gqa_attn_prefill_workspace_size(10, 5) == 0
+    assert binding.gqa_attn_prefill_workspace_size(512, 32768, paged=True, int8k=True) == 0
+
+
+def test_workspace_errors_return_before_launch():
+    # every case below is refused on the host, so no kernel is launched
+    assert ws_call(None, 0) == WORKSPACE
+    assert ws_call(4096, SPLIT_512x32768 - 1) == WORKSPACE
+    assert ws_call(4096 + 8, SPLIT_512x32768) == MISALIGNED
+    assert ws_call(4096, SPLIT_512x32768, q_len=10, kv_len=5) == BADLEN
+    lib = binding.library()
+    vp = ctypes.c_void_p
+    assert lib.gqa_attn_prefill_ws(None, vp(16), vp(16), None, 0, None, 512, 32768, vp(16),
+                                   vp(4096), SPLIT_512x32768, None) == NULL
+    # q_len == 0 is a no-op for the workspace form too
+    assert lib.gqa_attn_prefill_ws(None, None, None, None, 0, None, 0, 100, None, None, 0,
+                                   None) == OK
+
+
+def test_plan_reports_segments():
+    plan = binding.gqa_attn_prefill_plan(4096, 32768)
+    assert "segments=1 workspace_bytes=0" in plan
+    plan = binding.gqa_attn_prefill_plan(512, 32768, paged=True)
+    assert "workgroups=512" in plan and "segments=8" in plan
+    assert f"workspace_bytes={SPLIT_512x32768}" in plan

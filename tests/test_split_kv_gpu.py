@@ -1,0 +1,128 @@
+"""Parity of the KV-segment path (gqa_attn_prefill_ws) with the CPU oracle.
+
+When q_len is short the call cuts the history into KV segments, each workgroup
+writes an unnormalised partial output with its reference maximum and row sum, and a
+merge kernel combines them by the log-sum-exp rule. The result is the same softmax,
+so the bf16 tolerances of the unsplit path apply unchanged (max |err| <= 1e-2, mean
+|err| <= 1e-3 against the float64 oracle), element by element on every shape here.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_causal_prefill_amd as gqa
+import oracle
+from gqa_synth import block_table_for, make_qkv, scatter_paged
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+BF16_MAX, BF16_MEAN = 1e-2, 1e-3
+
+
+def note(msg):
+    print(msg, flush=True)
+
+
+def errors(out, ref):
+    e = np.abs(out.float().cpu().numpy().astype(np.float64) - ref)
+    return float(e.max()), float(e.mean())
+
+
+def segments(q_len, kv_len, paged=False):
+    plan = gqa.gqa_attn_prefill_plan(q_len, kv_len, paged=paged)
+    return int(plan.split("segments=")[1].split()[0])
+
+
+# (q_len, kv_len) -> segments: 8 KV segments for one token block, 5 for a ragged
+# 4-block chunk, 16 for a single query, 8 for 17 token blocks with a ragged last one
+SPLIT_SHAPES = [(32, 4096, 8), (100, 3000, 5), (1, 8192, 16), (513, 9000, 8)]
+
+
+@pytest.mark.parametrize("q_len,kv_len,nseg", SPLIT_SHAPES)
+def test_split_contiguous_full(q_len, kv_len, nseg):
+    note(f"case split contiguous {q_len}x{kv_len}")
+    assert segments(q_len, kv_len) == nseg
+    q, k, v, _ = make_qkv(q_len, kv_len, seed=5000 + q_len)
+    out = gqa.gqa_attn_prefill_ws(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    mx, mean = errors(out, oracle.attention(q, k, v))
+    note(f"  {nseg} segments: max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+def test_split_paged_full_and_bitwise_equal_to_contiguous():
+    q_len, kv_len, nb = 64, 5000, 400
+    note(f"case split paged {q_len}x{kv_len}")
+    assert segments(q_len, kv_len, paged=True) > 1
+    q, k, v, rng = make_qkv(q_len, kv_len, seed=5100)
+    bt = block_table_for(rng, kv_len, nb)
+    kc, vc = scatter_paged(k, bt, nb), scatter_paged(v, bt, nb)
+    out = gqa.gqa_attn_prefill_ws(q.to(DEV), kc.to(DEV), vc.to(DEV), block_table=bt.to(DEV),
+                                  kv_len=kv_len)
+    contig = gqa.gqa_attn_prefill_ws(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    mx, mean = errors(out, oracle.attention(q, k, v))
+    note(f"  max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+    assert torch.equal(out, contig)
+
+
+def test_split_restart_inside_a_segment():
+    """Keys from 1500 on score 144 (log2 units) above the rest: segment 2 (keys
+    1024..1535) must restart with its exact maxima, later segments take a high
+    reference from their first tile, and the merge weighs the low segments by ~2^-144."""
+    q_len, kv_len, start = 32, 4096, 1500
+    note("case split restart")
+    q, k, v, _ = make_qkv(q_len, kv_len, seed=5200)
+    q2, k2 = q.to(torch.float32).clone(), k.to(torch.float32).clone()
+    q2[..., 0] += 40.0
+    k2[start:, :, 0] = 40.0
+    q, k = q2.to(torch.bfloat16), k2.to(torch.bfloat16)
+    out = gqa.gqa_attn_prefill_ws(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    mx, mean = errors(out, oracle.attention(q, k, v))
+    note(f"  max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+def test_split_deterministic_and_close_to_unsplit():
+    note("case split determinism")
+    q, k, v, _ = make_qkv(40, 6000, seed=5300)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    a = gqa.gqa_attn_prefill_ws(qd, kd, vd)
+    b = gqa.gqa_attn_prefill_ws(qd, kd, vd)
+    c = gqa.gqa_attn_prefill(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    d = (a.float() - c.float()).abs()
+    note(f"  split vs unsplit: max {d.max().item():.3e}")
+    assert d.max().item() <= 2 * BF16_MAX
+
+
+def test_split_workspace_reused_for_a_smaller_call():
+    """One workspace sized for a large call serves a smaller one; its previous
+    contents do not leak into the result."""
+    note("case split workspace reuse")
+    big = gqa.gqa_attn_prefill_workspace_size(64, 8192)
+    ws = torch.full((big,), 0x7F, dtype=torch.uint8, device=DEV)   # NaN-like fill pattern
+    for q_len, kv_len, seed in [(64, 8192, 5400), (16, 2000, 5401)]:
+        assert 0 < gqa.gqa_attn_prefill_workspace_size(q_len, kv_len) <= big
+        q, k, v, _ = make_qkv(q_len, kv_len, seed=seed)
+        out = gqa.gqa_attn_prefill_ws(q.to(DEV), k.to(DEV), v.to(DEV), workspace=ws)
+        torch.cuda.synchronize()
+        mx, mean = errors(out, oracle.attention(q, k, v))
+        note(f"  {q_len}x{kv_len}: max {mx:.3e} mean {mean:.3e}")
+        assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+def test_unsplit_shapes_ignore_the_workspace():
+    """A grid that fills the chip runs in one piece: the workspace form returns the
+    plain call's bits."""
+    note("case no split")
+    q, k, v, _ = make_qkv(1024, 1500, seed=5500)
+    assert gqa.gqa_attn_prefill_workspace_size(1024, 1500) == 0
+    a = gqa.gqa_attn_prefill_ws(q.to(DEV), k.to(DEV), v.to(DEV))
+    b = gqa.gqa_attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
