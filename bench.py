@@ -35,8 +35,8 @@ KERNEL_SOURCE = os.path.join(ROOT, "gqa_causal_prefill_amd", "csrc", "gqa_prefil
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=3,
                     help="1 tiny, 2 4096x8192, 3 4096x32768 (default), 4 paged 512x32768, "
                          "5 int8-k 3072x16384, 6 4096x16384")

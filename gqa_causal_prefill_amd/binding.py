@@ -179,9 +179,10 @@ def gqa_attn_prefill_ws(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     splits, one is allocated through torch for this call."""
     args, out, (ql, kl, paged, int8k) = _prefill_args(q, k, v, block_table, num_blocks,
                                                       k_scale, q_len, kv_len, out)
-    need = gqa_attn_prefill_workspace_size(ql, kl, paged, int8k)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        need = gqa_attn_prefill_workspace_size(ql, kl, paged, int8k)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         if workspace.device != q.device or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous tensor on " + str(q.device))

@@ -1015,18 +1015,51 @@ Launch shape_launch(int32_t q_len, bool int8k) {
 constexpr int kCUs = 256;        // compute units of an MI355X
 constexpr int kMinSegTiles = 8;  // shortest KV segment (512 keys)
 
-// KV segments per (KV head, token block) for a call that has a workspace: 1 while the
-// unsplit grid already gives every CU a workgroup, else enough segments for about two
-// workgroups per CU, each at least kMinSegTiles tiles long in the shortest (first) token
-// block. INT8 keys are not split: each segment would quantise its query rows again,
-// which the pages keep to once per row ("gfx936 DCU上实现INT8 QK MMAC" §4).
+// Estimated run time, in tile times (one workgroup through one 64-key tile), of a launch
+// that cuts every (KV head, token block) into n_seg KV segments. The workgroups run
+// longest first, one per compute unit, so they go in rounds of kCUs and each round
+// lasts about as long as its first (longest) workgroup; each workgroup also pays about
+// two tile times of prologue and epilogue; and a split launch moves n_seg partial rows
+// of 1 KiB + 8 B per output row through memory twice (written, then read by the merge)
+// at about 5 TB/s, against the ~2.4 us a workgroup spends on one tile.
+double plan_cost(int32_t q_len, int32_t kv_len, int n_tblk, int n_seg) {
+  constexpr double kWgTiles = 2.0;
+  const int tok = Shape<GQA_DEFAULT_QB>::kTokPerWg;
+  const int64_t pieces = (int64_t)kHkv * n_tblk * n_seg;
+  double t = 0.0;
+  for (int64_t first = 0; first < pieces; first += kCUs) {
+    const int64_t tblk = n_tblk - 1 - first / n_seg / kHkv;   // grid order: longest first
+    const int64_t last = std::min<int64_t>((tblk + 1) * tok, q_len);
+    const int64_t T = ((int64_t)kv_len - q_len + last + kKt - 1) / kKt;
+    t += (double)((T + n_seg - 1) / n_seg) + kWgTiles;
+  }
+  if (n_seg > 1) t += 2.0 * n_seg * (double)q_len * kHq * (kD + 2) * 4 / (5e12 * 2.4e-6);
+  return t;
+}
+
+// KV segments per (KV head, token block) for a call that has a workspace. A grid with a
+// workgroup for every compute unit is not split (its longest-first order balances it,
+// and splitting it further was measured to gain nothing). A smaller grid takes the
+// count with the lowest plan_cost among those that keep every segment at least
+// kMinSegTiles long in the shortest (first) token block.
 int segments_for(int32_t q_len, int32_t kv_len, bool int8k, int unsplit_workgroups) {
-  if (int8k || unsplit_workgroups >= kCUs || q_len == 0) return 1;
-  const int first_tok_block = std::min<int32_t>(q_len, Shape<GQA_DEFAULT_QB>::kTokPerWg);
-  const int64_t t_min = ((int64_t)kv_len - q_len + first_tok_block + kKt - 1) / kKt;
-  int n = (2 * kCUs + unsplit_workgroups - 1) / unsplit_workgroups;
-  n = (int)std::min<int64_t>(n, t_min / kMinSegTiles);
-  return std::max(n, 1);
+  (void)int8k;
+  if (q_len == 0 || unsplit_workgroups >= kCUs) return 1;
+  const int tok = Shape<GQA_DEFAULT_QB>::kTokPerWg;
+  const int n_tblk = (q_len + tok - 1) / tok;
+  const int64_t t_min = ((int64_t)kv_len - q_len + std::min(q_len, tok) + kKt - 1) / kKt;
+  int best = 1;
+  double best_cost = plan_cost(q_len, kv_len, n_tblk, 1);
+  static const int kCandidates[] = {2, 3, 4, 5, 6, 8, 10, 12, 16, 24, 32, 48, 64};
+  for (int n : kCandidates) {
+    if (t_min / n < kMinSegTiles) break;
+    const double c = plan_cost(q_len, kv_len, n_tblk, n);
+    if (c < 0.97 * best_cost) {   // split only for a clear gain
+      best = n;
+      best_cost = c;
+    }
+  }
+  return best;
 }
 
 size_t workspace_bytes_for(int32_t q_len, int n_seg) {

@@ -108,11 +108,12 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v,
  *
  * Long histories may be cut into KV segments, as the pages do for decode attention
  * and for chunked prefill with history ("gfx936 DCU上实现INT8 QK MMAC" §4): this
- * happens when q_len is so short that one workgroup per (KV head, 32 query tokens)
- * would leave compute units idle. Each segment then writes its unnormalised output,
- * its per-row reference maximum and row sum to the workspace, and a merge step
- * combines them by the log-sum-exp rule into `out`. INT8 keys are never split (each
- * segment would quantise the query rows again).
+ * happens when one workgroup per (KV head, 32 query tokens) would leave compute
+ * units idle (fewer workgroups than CUs; the segment count comes from an estimate of
+ * the launch's run time). Each segment then
+ * writes its unnormalised output, its per-row reference maximum and row sum to the
+ * workspace, and a merge step combines them by the log-sum-exp rule into `out`.
+ * With INT8 keys every segment quantises its query rows itself (same codes).
  *
  * paged, int8k: 0 or 1. Pure host function. Returns 0 for arguments
  * gqa_attn_prefill_ws would refuse.

@@ -144,18 +144,21 @@ def ws_call(ws, ws_bytes, q_len=512, kv_len=32768, bt=None, nb=0):
                                    vp(16), vp(ws), ws_bytes, None)
 
 
-SPLIT_512x32768 = 8 * 512 * 24 * (256 + 2) * 4   # 8 segments of fp32 (O, m, l) per row
+SPLIT_512x32768 = 4 * 512 * 24 * (256 + 2) * 4   # 4 segments of fp32 (O, m, l) per row
 
 
 def test_workspace_size():
-    # a grid that fills the chip runs unsplit and needs nothing
+    # grids that balance by their longest-first order run unsplit and need nothing
     assert binding.gqa_attn_prefill_workspace_size(4096, 32768) == 0
-    assert binding.gqa_attn_prefill_workspace_size(3072, 16384, int8k=True) == 0
-    # 512 queries: 4 KV heads x 16 token blocks = 64 workgroups -> 8 segments of 63 tiles
+    assert binding.gqa_attn_prefill_workspace_size(4096, 8192) == 0
+    assert binding.gqa_attn_prefill_workspace_size(2048, 32768) == 0   # one full round
+    # 512 queries: 4 KV heads x 16 token blocks = 64 workgroups -> 4 segments of ~126 tiles
     assert binding.gqa_attn_prefill_workspace_size(512, 32768) == SPLIT_512x32768
     assert binding.gqa_attn_prefill_workspace_size(512, 32768, paged=True) == SPLIT_512x32768
-    # INT8 keys are never split; short histories are not split below 8 tiles a segment
-    assert binding.gqa_attn_prefill_workspace_size(512, 32768, int8k=True) == 0
+    assert binding.gqa_attn_prefill_workspace_size(512, 32768, int8k=True) == SPLIT_512x32768
+    # a grid with a workgroup for every CU is not split (3072 queries: 384 workgroups)
+    assert binding.gqa_attn_prefill_workspace_size(3072, 16384, int8k=True) == 0
+    # short histories are not split below 8 tiles a segment
     assert binding.gqa_attn_prefill_workspace_size(32, 500) == 0
     # arguments the call would refuse
     assert binding.gqa_attn_prefill_workspace_size(10, 5) == 0
@@ -181,5 +184,5 @@ def test_plan_reports_segments():
     plan = binding.gqa_attn_prefill_plan(4096, 32768)
     assert "segments=1 workspace_bytes=0" in plan
     plan = binding.gqa_attn_prefill_plan(512, 32768, paged=True)
-    assert "workgroups=512" in plan and "segments=8" in plan
+    assert "workgroups=256" in plan and "segments=4" in plan
     assert f"workspace_bytes={SPLIT_512x32768}" in plan

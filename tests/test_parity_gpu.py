@@ -233,7 +233,7 @@ def test_full_size_int8k_sampled():
     torch.cuda.synchronize()
     assert np.array_equal(gq.cpu().numpy(), kq) and np.array_equal(gs.cpu().numpy(), ks)
     note(f"case {w.name}: running")
-    out = gqa.gqa_attn_prefill(d["q"].to(DEV), gq, d["v"].to(DEV), k_scale=gs)
+    out = gqa.gqa_attn_prefill_ws(d["q"].to(DEV), gq, d["v"].to(DEV), k_scale=gs)
     torch.cuda.synchronize()
     rows = sample_rows(w.q_len, seed=5)
     ref = oracle.attention_int8k(d["q"], kq, ks, d["v"], rows=rows)

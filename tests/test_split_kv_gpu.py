@@ -35,8 +35,8 @@ def segments(q_len, kv_len, paged=False):
 
 
 # (q_len, kv_len) -> segments: 8 KV segments for one token block, 5 for a ragged
-# 4-block chunk, 16 for a single query, 8 for 17 token blocks with a ragged last one
-SPLIT_SHAPES = [(32, 4096, 8), (100, 3000, 5), (1, 8192, 16), (513, 9000, 8)]
+# 4-block chunk, 16 for a single query, 3 for 17 token blocks with a ragged last one
+SPLIT_SHAPES = [(32, 4096, 8), (100, 3000, 5), (1, 8192, 16), (513, 9000, 3)]
 
 
 @pytest.mark.parametrize("q_len,kv_len,nseg", SPLIT_SHAPES)
@@ -126,3 +126,21 @@ def test_unsplit_shapes_ignore_the_workspace():
     b = gqa.gqa_attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV))
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("q_len,kv_len", [(64, 3000), (200, 4000)])
+def test_split_int8k_full(q_len, kv_len):
+    """INT8 keys through KV segments: every segment quantises its query rows itself,
+    with the same codes, so the INT8 bound of the unsplit path applies."""
+    note(f"case split int8k {q_len}x{kv_len}")
+    plan = gqa.gqa_attn_prefill_plan(q_len, kv_len, int8k=True)
+    assert int(plan.split("segments=")[1].split()[0]) > 1
+    q, k, v, _ = make_qkv(q_len, kv_len, seed=5600 + q_len)
+    kq, ks = oracle.quantize_rows_int8(k)
+    out = gqa.gqa_attn_prefill_ws(q.to(DEV), torch.from_numpy(kq).to(DEV), v.to(DEV),
+                                  k_scale=torch.from_numpy(ks).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.attention_int8k(q, kq, ks, v)
+    e = np.abs(out.float().cpu().numpy().astype(np.float64) - ref)
+    note(f"  max {e.max():.3e}")
+    assert e.max() <= 2e-3
