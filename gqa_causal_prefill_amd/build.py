@@ -19,6 +19,9 @@ INCLUDE = os.path.join(ROOT, "include")
 
 LIB = os.path.join(PKG, "libgqa_prefill.so")
 PROBE_LIB = os.path.join(PKG, "libgqa_layout_probe.so")
+# the same library with 32 query columns per wave (64 tokens x 2 heads per workgroup)
+# instead of 48: tests compare the two for bitwise-identical output
+QB2_LIB = os.path.join(PKG, "libgqa_prefill_qb2.so")
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in any generated code.
 # -amdgpu-mfma-vgpr-form: MFMA accumulators in architectural VGPRs where they fit. The
@@ -44,8 +47,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def _compile(sources, output, verbose=False):
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", "-o", output + ".tmp", *sources]
+def _compile(sources, output, verbose=False, defines=()):
+    cmd = [hipcc(), *HIPCC_FLAGS, *defines, f"-I{INCLUDE}", "-o", output + ".tmp", *sources]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines()
             if "not a recognized feature" not in ln]
@@ -57,8 +60,9 @@ def _compile(sources, output, verbose=False):
 
 
 def build(verbose: bool = False) -> None:
-    """Compile both libraries (always, even if they exist)."""
+    """Compile the libraries (always, even if they exist)."""
     _compile([os.path.join(CSRC, "gqa_prefill.hip")], LIB, verbose)
+    _compile([os.path.join(CSRC, "gqa_prefill.hip")], QB2_LIB, verbose, ("-DGQA_DEFAULT_QB=2",))
     _compile([os.path.join(CSRC, "layout_probe.hip")], PROBE_LIB, verbose)
 
 

@@ -375,7 +375,7 @@ __device__ __forceinline__ bf16x8 vt_value(const VtFrag& f) {
 // V^T fragment (ks, db) sits at vbase[db & 3] + (db >> 2) * kSegStride + ks * 4096.
 // Fragments travel in a ring of kVtDepth + 1: step N issues the reads of step
 // N + kVtDepth, then waits for its own (2 reads per step).
-constexpr int kVtDepth = 6;   // at most 2 (kVtDepth + 1) = 14 reads in flight: lgkmcnt counts to 15
+constexpr int kVtDepth = 3;   // at most 2 (kVtDepth + 1) = 8 reads in flight (lgkmcnt counts to 15)
 
 template <int N>
 __device__ __forceinline__ void vt_issue_step(VtFrag& f, const uint32_t (&vbase)[4]) {
@@ -658,6 +658,10 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
           for (int r = 0; r < 4; ++r) sc[b][4 * kk + r] = sacc[b][2 * h + kk][r];
       }
     } else {
+      // The score is rounded once as float(S) * (sK * sQ * log2(e)/16) and only then
+      // offset by the maximum: no fusing of this product into a later add, so every
+      // build (whatever it schedules around this code) rounds every score the same way.
+#pragma clang fp contract(off)
       // scales of keys 16 (2 h + kk) + 4 L .. + 3 for KV head g
       u32x4 sr[2];
       const uint32_t a = sk_slot + 2 * h * 256 + g * 64 + 16 * L;
@@ -746,10 +750,11 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       const int kbase = j * kKt;
       const uint8_t* knext = smem + ((j + 1) & 1) * kKTile;             // K(j+1) (stale on the last tile)
       const uint8_t* vcur = smem + kVOff + (j & 1) * 4 * kSegStride;   // V(j)
-      // copies of K(j+2) and V(j+1), spread evenly over the K steps of both halves and
-      // the first 24 P·V steps: the vector memory path moves about 64 B per clock per
-      // CU, so the 64 KiB of a tile need a good part of the iteration, and issuing them
-      // in a burst would stall the waves on a full address queue
+      // copies of K(j+2) and V(j+1), spread evenly over the K steps of both halves (one
+      // per step for bf16 keys): the vector memory path moves about 64 B per clock per CU,
+      // so the 64 KiB of a tile need a good part of the iteration, and issuing them in a
+      // burst would stall the waves on a full address queue; the P·V steps, three MFMAs
+      // each, leave too little time between copies (measured)
       // (a tile past the segment is fetched from kv_len on: no rows, no traffic)
       const int kb2 = j + 2 < j1 ? kbase + 2 * kKt : p.kv_len;
       const int kb1 = j + 1 < j1 ? kbase + kKt : p.kv_len;
@@ -767,7 +772,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
         else
           scp.issue(svo);
       };
-      constexpr int kSlots = 2 * Q::kSteps + 24;   // issue slots: K steps, then P·V steps
+      constexpr int kSlots = 2 * Q::kSteps;   // issue slots: the K steps of both halves
       // the copies whose slot (I * kSlots) / kCopies is SLOT
       auto copies_at = [&](auto slot_c) {
         constexpr int kSlot = decltype(slot_c)::value;
@@ -821,9 +826,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
         static_for<0, kVtDepth>([&](auto nc) {   // the first kVtDepth steps' reads
           vt_issue_step<decltype(nc)::value>(vf[decltype(nc)::value], vbase);
         });
-        PvStep<0, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc, [&](auto nc) {
-          copies_at(std::integral_constant<int, 2 * Q::kSteps + decltype(nc)::value>{});
-        });
+        PvStep<0, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc, [](auto) {});
       }
 
       // Flags are double-buffered by tile parity: the write for tile j + 2 happens only
