@@ -18,6 +18,10 @@ heads, head_dim 256, BF16):
   ``cache[block_table[t // 16], :, t % 16, :]``. Physical blocks that the table
   does not use and slots past kv_len - 1 are filled with a large sentinel pattern
   (+/-64 and 0) so that a wrong gather shows up in the output.
+* paged INT8 keys: the codes of the logical K go to the split-d cache
+  ``[num_blocks, 4, 16, 16, 16]`` (feature f of key t at
+  ``[block_table[t // 16], h, f // 16, t % 16, f % 16]``) and their scales to a paged
+  scale cache ``[num_blocks, 4, 16]`` whose unused entries are NaN.
 """
 
 from __future__ import annotations
@@ -102,6 +106,30 @@ def scatter_paged(x: torch.Tensor, block_table: torch.Tensor, num_blocks: int) -
     cache[block_table.long()] = padded.view(n, BLOCK_SIZE, HKV, D).permute(0, 2, 1, 3)
     last_used = kv_len - (n - 1) * BLOCK_SIZE
     cache[block_table[-1].item(), :, last_used:, :] = tail[:, last_used:, :]
+    return cache
+
+
+def scatter_paged_int8_splitd(kq: torch.Tensor, block_table: torch.Tensor,
+                              num_blocks: int) -> torch.Tensor:
+    """Place logical INT8 K codes [kv_len, 4, 256] into the split-d paged cache
+    [num_blocks, 4, 16, 16, 16]: feature f of key t, head h goes to
+    [block_table[t // 16], h, f // 16, t % 16, f % 16]. Unused memory holds the
+    sentinel pattern."""
+    rows = scatter_paged(kq, block_table, num_blocks)          # [nb, 4, 16 slots, 256]
+    return rows.view(num_blocks, HKV, BLOCK_SIZE, D // 16, 16).permute(0, 1, 3, 2, 4).contiguous()
+
+
+def scatter_paged_scales(ks: torch.Tensor, block_table: torch.Tensor,
+                         num_blocks: int) -> torch.Tensor:
+    """Place per-token key scales [kv_len, 4] (float32) into a paged scale cache
+    [num_blocks, 4, 16]: the scale of key t, head h goes to
+    [block_table[t // 16], h, t % 16]. Every other entry is NaN, so a scale that the
+    computation should never use poisons the result if it is read."""
+    kv_len = ks.shape[0]
+    cache = torch.full((num_blocks, HKV, BLOCK_SIZE), float("nan"), dtype=torch.float32)
+    for t0 in range(0, kv_len, BLOCK_SIZE):
+        n = min(BLOCK_SIZE, kv_len - t0)
+        cache[int(block_table[t0 // BLOCK_SIZE]), :, :n] = ks[t0:t0 + n].T
     return cache
 
 

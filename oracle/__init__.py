@@ -41,6 +41,8 @@ from .prefill import (  # noqa: F401
     attention_int8k,
     causal_limit,
     gather_paged,
+    gather_paged_int8_splitd,
+    gather_paged_scales,
     kv_head_of,
     quantize_rows_int8,
     score_matrix,

@@ -156,6 +156,53 @@ def gather_paged(cache, block_table, kv_len: int) -> np.ndarray:
     return out
 
 
+def gather_paged_int8_splitd(cache, block_table, kv_len: int) -> np.ndarray:
+    """Logical INT8 K codes [kv_len, 4, 256] read back from the split-d paged cache.
+
+    cache: [num_blocks, 4, 256 / 16, 16, 16] -- per (block, KV head) the 256 features
+    of its 16 slots are stored as 16 chunks of 16 features, chunk-major, so that a
+    chunk of all 16 slots is contiguous [INT8 QK §3: K cache [block, kv_head,
+    head_dim / 16, block_size, 16]]. Feature f of logical key t, KV head h is
+    cache[block_table[t // 16], h, f // 16, t % 16, f % 16]. Codes are returned in
+    the cache's dtype (exact).
+    """
+    cache = np.asarray(cache.cpu() if hasattr(cache, "cpu") else cache)
+    bt = np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table,
+                    dtype=np.int64)
+    nb = cache.shape[0]
+    if cache.shape[1:] != (HKV, D // 16, BLOCK_SIZE, 16):
+        raise ValueError(f"split-d cache must be [blocks, {HKV}, {D // 16}, {BLOCK_SIZE}, 16]")
+    out = np.empty((kv_len, HKV, D), dtype=cache.dtype)
+    for t in range(kv_len):
+        blk = bt[t // BLOCK_SIZE]
+        if not 0 <= blk < nb:
+            raise IndexError(f"block table entry {blk} out of range for {nb} blocks")
+        slot = t % BLOCK_SIZE
+        for h in range(HKV):
+            for c in range(D // 16):
+                out[t, h, 16 * c:16 * c + 16] = cache[blk, h, c, slot, :]
+    return out
+
+
+def gather_paged_scales(scale_cache, block_table, kv_len: int) -> np.ndarray:
+    """Per-token key scales [kv_len, 4] read back from a paged scale cache [num_blocks,
+    4, 16]: the scale of logical key t, KV head h is scale_cache[block_table[t // 16],
+    h, t % 16] (the scales live in the same pages as their keys' codes)."""
+    sc = np.asarray(scale_cache.cpu() if hasattr(scale_cache, "cpu") else scale_cache)
+    bt = np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table,
+                    dtype=np.int64)
+    nb = sc.shape[0]
+    if sc.shape[1:] != (HKV, BLOCK_SIZE):
+        raise ValueError(f"paged scale cache must be [blocks, {HKV}, {BLOCK_SIZE}]")
+    out = np.empty((kv_len, HKV), dtype=sc.dtype)
+    for t in range(kv_len):
+        blk = bt[t // BLOCK_SIZE]
+        if not 0 <= blk < nb:
+            raise IndexError(f"block table entry {blk} out of range for {nb} blocks")
+        out[t] = sc[blk, :, t % BLOCK_SIZE]
+    return out
+
+
 def quantize_rows_int8(x):
     """Symmetric dynamic INT8 quantisation of each 256-element row [INT8 QK §1, §4].
 

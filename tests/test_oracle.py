@@ -133,6 +133,76 @@ def test_golden_paged_gather_hand_example():
     assert len(spec["keys"]) == kv_len
 
 
+def load_splitd_example():
+    spec = {"k": [], "s": []}
+    with open(os.path.join(GOLDEN, "paged_int8_splitd_hand_example.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            tok = line.split()
+            if tok[0] in ("kv_len", "num_blocks"):
+                spec[tok[0]] = int(tok[1])
+            elif tok[0] == "block_table":
+                spec["block_table"] = [int(x) for x in tok[1:]]
+            elif tok[0] == "k":
+                spec["k"].append(tuple(int(x) for x in tok[1:]))
+            elif tok[0] == "s":
+                spec["s"].append(tuple(int(x) for x in tok[1:]))
+    return spec
+
+
+def test_golden_paged_int8_splitd_hand_example():
+    """INT8 QK §3's split-d paged K layout and the paged scales, against positions
+    worked out by hand."""
+    spec = load_splitd_example()
+    nb, kv_len, bt = spec["num_blocks"], spec["kv_len"], np.array(spec["block_table"])
+    b, h, c, sl, e = np.meshgrid(np.arange(nb), np.arange(HKV), np.arange(D // 16), np.arange(16),
+                                 np.arange(16), indexing="ij")
+    kcache = b * 65536 + h * 4096 + c * 256 + sl * 16 + e
+    b2, h2, s2 = np.meshgrid(np.arange(nb), np.arange(HKV), np.arange(16), indexing="ij")
+    scache = (b2 * 100 + h2 * 10 + s2).astype(np.float64)
+    k = oracle.gather_paged_int8_splitd(kcache, bt, kv_len)
+    sc = oracle.gather_paged_scales(scache, bt, kv_len)
+    assert k.shape == (kv_len, HKV, D) and sc.shape == (kv_len, HKV)
+    for t, hh, f, want in spec["k"]:
+        assert k[t, hh, f] == want, (t, hh, f)
+    for t, hh, want in spec["s"]:
+        assert sc[t, hh] == want, (t, hh)
+
+
+def test_splitd_gather_equals_rowmajor_gather():
+    """The split-d cache holds the same rows as a [block, head, slot, 256] cache whose row
+    (block, head, slot) is the concatenation of its 16 chunks; both gathers agree."""
+    rng = np.random.default_rng(7)
+    nb, kv_len = 6, 83
+    kc = rng.integers(-127, 128, (nb, HKV, D // 16, 16, 16)).astype(np.int8)
+    rows = np.zeros((nb, HKV, 16, D), np.int8)
+    for c in range(D // 16):
+        rows[:, :, :, 16 * c:16 * c + 16] = kc[:, :, c, :, :]
+    bt = rng.permutation(nb)
+    got = oracle.gather_paged_int8_splitd(kc, bt, kv_len)
+    want = oracle.gather_paged(rows, bt, kv_len)
+    assert got.dtype == np.int8
+    np.testing.assert_array_equal(got.astype(np.float64), want)
+
+
+def test_splitd_generator_round_trip():
+    """The input generator's split-d placement is what the oracle's gather reads back,
+    and every scale slot the keys do not use is NaN."""
+    from gqa_synth import scatter_paged_int8_splitd, scatter_paged_scales
+    rng = np.random.default_rng(8)
+    kv_len, nb = 37, 5
+    kq = torch.from_numpy(rng.integers(-127, 128, (kv_len, HKV, D)).astype(np.int8))
+    ks = torch.from_numpy(rng.random((kv_len, HKV), dtype=np.float32))
+    bt = block_table_for(rng, kv_len, nb)
+    kc, sc = scatter_paged_int8_splitd(kq, bt, nb), scatter_paged_scales(ks, bt, nb)
+    assert kc.shape == (nb, HKV, D // 16, 16, 16) and kc.dtype == torch.int8
+    np.testing.assert_array_equal(oracle.gather_paged_int8_splitd(kc, bt, kv_len), kq.numpy())
+    np.testing.assert_array_equal(oracle.gather_paged_scales(sc, bt, kv_len), ks.numpy())
+    assert int(torch.isnan(sc).sum()) == (nb * 16 - kv_len) * HKV
+
+
 # ----------------------------------------------------------------------------- brute force
 
 def brute_force(q, k, v):
