@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=3,
                     help="1 tiny, 2 4096x8192, 3 4096x32768 (default), 4 paged 512x32768, "
-                         "5 int8-k 3072x16384, 6 4096x16384")
+                         "5 int8-k 3072x16384, 6 4096x16384, 7 paged int8-k 512x32768")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="query rows of the workload the CPU oracle computes (all 24 heads)")
@@ -111,7 +111,14 @@ def main():
     q = d["q"].to(dev)
     v = (d["v_cache"] if w.paged else d["v"]).to(dev)
     kw = {}
-    if w.paged:
+    if w.paged and w.int8k:
+        from gqa_synth import scatter_paged_int8_splitd, scatter_paged_scales
+        kq, ks = gqa.gqa_quantize_rows_int8(d["k"].to(dev))
+        torch.cuda.synchronize()
+        k = scatter_paged_int8_splitd(kq.cpu(), d["block_table"], w.num_blocks).to(dev)
+        kw = dict(block_table=d["block_table"].to(dev), kv_len=w.kv_len,
+                  k_scale=scatter_paged_scales(ks.cpu(), d["block_table"], w.num_blocks).to(dev))
+    elif w.paged:
         k = d["k_cache"].to(dev)
         kw = dict(block_table=d["block_table"].to(dev), kv_len=w.kv_len)
     elif w.int8k:
@@ -177,7 +184,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "q_len": w.q_len, "kv_len": w.kv_len, "q_heads": HQ,
                    "kv_heads": HKV, "head_dim": D,
-                   "kv_layout": "paged16" if w.paged else "contiguous",
+                   "kv_layout": ("paged16_splitd" if w.int8k else "paged16") if w.paged else "contiguous",
                    "keys": "int8" if w.int8k else "bf16",
                    "variant": gqa.gqa_attn_prefill_plan(w.q_len, w.kv_len, w.paged, w.int8k)},
         "roofline": roofline,

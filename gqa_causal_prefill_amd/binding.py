@@ -129,8 +129,10 @@ def _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out)
             raise ValueError("kv_len is required with a block table")
         nb = k.shape[0] if num_blocks is None else num_blocks
         _expect(block_table, "block_table", torch.int32, (math.ceil(kv_len / BLOCK_SIZE),), dev)
-        cache_shape = (nb, NUM_KV_HEADS, BLOCK_SIZE, HEAD_DIM)
-        k_shape = v_shape = cache_shape
+        v_shape = (nb, NUM_KV_HEADS, BLOCK_SIZE, HEAD_DIM)
+        # INT8 keys use the split-d page layout [block, kv_head, 256 / 16, 16, 16]
+        k_shape = ((nb, NUM_KV_HEADS, HEAD_DIM // 16, BLOCK_SIZE, 16) if k_scale is not None
+                   else v_shape)
     else:
         kv_len = k.shape[0] if kv_len is None else kv_len
         nb = 0
@@ -139,7 +141,8 @@ def _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out)
     _expect(k, "k", torch.int8 if k_scale is not None else torch.bfloat16, k_shape, dev)
     _expect(v, "v", torch.bfloat16, v_shape, dev)
     if k_scale is not None:
-        _expect(k_scale, "k_scale", torch.float32, (kv_len, NUM_KV_HEADS), dev)
+        ks_shape = (nb, NUM_KV_HEADS, BLOCK_SIZE) if paged else (kv_len, NUM_KV_HEADS)
+        _expect(k_scale, "k_scale", torch.float32, ks_shape, dev)
     if out is None:
         out = torch.empty((q_len, NUM_Q_HEADS, HEAD_DIM), dtype=torch.bfloat16, device=dev)
     else:
@@ -159,7 +162,9 @@ def gqa_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     q: bf16 [q_len, 24, 256]. Contiguous: k, v [kv_len, 4, 256]. Paged (block_table
     given): k, v caches [num_blocks, 4, 16, 256] and block_table int32
     [ceil(kv_len / 16)] (kv_len must then be given). INT8 keys: k int8 and
-    k_scale float32 [kv_len, 4]. Returns out (bf16 [q_len, 24, 256]).
+    k_scale float32 [kv_len, 4]; paged, k is the split-d cache int8
+    [num_blocks, 4, 16, 16, 16] and k_scale float32 [num_blocks, 4, 16].
+    Returns out (bf16 [q_len, 24, 256]).
     """
     args, out, _ = _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out)
     st = library().gqa_attn_prefill(*args, _stream_handle(q, stream))

@@ -188,11 +188,21 @@ __device__ __forceinline__ lds_void* lds_ptr(uint32_t addr) {
   return (lds_void*)(uintptr_t)addr;
 }
 
-template <bool PAGED, int ROW_BYTES, bool V>
+// SPLITD: the paged INT8 K cache of "gfx936 DCU上实现INT8 QK MMAC" §3, laid out
+// [block, kv_head, 256 / 16, 16 slots, 16]: a (block, head) page is 16 chunks of 16
+// features, each holding that chunk for all 16 slots. Feature chunk c of slot k sits at
+// c * 256 + k * 16 in the page, so a 128-byte segment (8 chunks) of a key row is read
+// from 8 places 256 bytes apart and consecutive segments are 2048 bytes apart. The
+// slots of a page are interleaved, so the descriptor covers the whole 4 KiB page; slots
+// past kv_len hold whatever the cache holds (finite int8 codes) and their scales, which
+// are zeroed (ScaleCopy), make their scores 0 before the causal mask hides them.
+template <bool PAGED, int ROW_BYTES, bool V, bool SPLITD = false>
 struct WaveCopy {
+  static_assert(!SPLITD || (PAGED && ROW_BYTES == kD), "the split-d layout is the paged INT8 K cache");
   static constexpr int kNseg = ROW_BYTES / 128;                      // 128-byte segments per row
   static constexpr int kInsts = 2 * kNseg;                          // 8 keys x one segment each
   static constexpr int kStride = PAGED ? ROW_BYTES : kHkv * ROW_BYTES;   // bytes between keys
+  static constexpr int kSegSrc = SPLITD ? 8 * kBs * 16 : 128;      // source bytes between segments
 
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t lds;   // LDS address of the wave's first row, segment 0, in the destination tile
@@ -201,15 +211,24 @@ struct WaveCopy {
   // the lane fetches the logical piece that the tile swizzle stores at position pp.
   static __device__ __forceinline__ uint32_t lane_offset(int lane, int half) {
     const int kr = lane >> 3, pp = lane & 7;
-    return (uint32_t)((8 * half + kr) * kStride + ((pp ^ tile_swizzle<V>(kr)) << 4));
+    const int piece = pp ^ tile_swizzle<V>(kr);
+    if constexpr (SPLITD)
+      return (uint32_t)(piece * kBs * 16 + (8 * half + kr) * 16);
+    else
+      return (uint32_t)((8 * half + kr) * kStride + (piece << 4));
   }
 
   // first = kbase + 16 w (wave-uniform); lds_rows = destination tile + 16 w rows
   __device__ __forceinline__ WaveCopy(const Params& p, const uint8_t* base, int g, int first,
                                       uint32_t lds_rows) {
     const int n = min(max(p.kv_len - first, 0), 16);   // rows of this wave before kv_len
+    int bytes;
+    if constexpr (SPLITD)
+      bytes = n > 0 ? kBs * ROW_BYTES : 0;
+    else
+      bytes = n > 0 ? (n - 1) * kStride + ROW_BYTES : 0;
     // (uniform; readfirstlane keeps the whole descriptor in scalar registers)
-    const int nrec = __builtin_amdgcn_readfirstlane(n > 0 ? (n - 1) * kStride + ROW_BYTES : 0);
+    const int nrec = __builtin_amdgcn_readfirstlane(bytes);
     const uint8_t* wb;
     if constexpr (PAGED) {
       const int blk = min(max(p.bt[min(first, p.kv_len - 1) >> 4], 0), p.num_blocks - 1);
@@ -226,27 +245,47 @@ struct WaveCopy {
   __device__ __forceinline__ void issue(const uint32_t (&voff)[2]) const {
     constexpr int half = I / kNseg, sg = I % kNseg;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds + half * 1024 + sg * kSegStride), 16,
-                                             voff[half], sg * 128, 0, 0);
+                                             voff[half], sg * kSegSrc, 0, 0);
   }
 };
 
 // INT8 key scales: each wave copies the scales of its 16 keys for all 4 KV heads into
 // a 1 KiB slot laid out [16-key block][KV head][16 keys] (lane = 16 head + key).
+// Contiguous scales are [kv_len, 4]; paged ones [block, 4, 16], the 256 bytes of a
+// block in lane order. Scales of keys past kv_len arrive as 0: out of the descriptor's
+// range (contiguous), or through an out-of-range lane offset (paged, where a block's
+// slots are interleaved by head).
+template <bool PAGED>
 struct ScaleCopy {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t lds;
+  int n;   // keys of this wave before kv_len
   __device__ __forceinline__ ScaleCopy() = default;
   static __device__ __forceinline__ uint32_t lane_offset(int lane) {
-    return (uint32_t)((lane & 15) * kHkv * 4 + (lane >> 4) * 4);
+    if constexpr (PAGED)
+      return (uint32_t)(lane * 4);
+    else
+      return (uint32_t)((lane & 15) * kHkv * 4 + (lane >> 4) * 4);
   }
   __device__ __forceinline__ ScaleCopy(const Params& p, int first, uint32_t lds_block) {
-    const int n = min(max(p.kv_len - first, 0), 16);
-    const uint8_t* wb = reinterpret_cast<const uint8_t*>(p.ks) + (size_t)first * kHkv * 4;
+    n = __builtin_amdgcn_readfirstlane(min(max(p.kv_len - first, 0), 16));
+    const uint8_t* wb;
+    int bytes;
+    if constexpr (PAGED) {
+      const int blk = min(max(p.bt[min(first, p.kv_len - 1) >> 4], 0), p.num_blocks - 1);
+      wb = reinterpret_cast<const uint8_t*>(p.ks) + (size_t)blk * kHkv * kBs * 4;
+      bytes = n > 0 ? kHkv * kBs * 4 : 0;
+    } else {
+      wb = reinterpret_cast<const uint8_t*>(p.ks) + (size_t)first * kHkv * 4;
+      bytes = n * kHkv * 4;
+    }
     rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wb), (short)0,
-                                             __builtin_amdgcn_readfirstlane(n * kHkv * 4), 0x00020000);
+                                             __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
     lds = lds_block;
   }
-  __device__ __forceinline__ void issue(uint32_t voff) const {
+  // voff = lane_offset(lane); key = lane % 16
+  __device__ __forceinline__ void issue(uint32_t voff, int key) const {
+    if constexpr (PAGED) voff = key < n ? voff : 0x40000000u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds), 4, voff, 0, 0, 0);
   }
 };
@@ -525,13 +564,15 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   }
 
   // ---- tile copies (this wave's 16 keys of each tile) ----
-  using KCopy = WaveCopy<PAGED, INT8K ? kD : 2 * kD, false>;
+  using KCopy = WaveCopy<PAGED, INT8K ? kD : 2 * kD, false, PAGED && INT8K>;
+  using SCopy = ScaleCopy<PAGED>;
   using VCopy = WaveCopy<PAGED, 2 * kD, true>;
   const uint32_t smem_addr = lds_addr(smem);
   const uint32_t sk_addr = smem_addr + kSkOff;   // key-scale ring (INT8 keys)
   const uint32_t kvo[2] = {KCopy::lane_offset(lane, 0), KCopy::lane_offset(lane, 1)};
   const uint32_t vvo[2] = {VCopy::lane_offset(lane, 0), VCopy::lane_offset(lane, 1)};
-  const uint32_t svo = ScaleCopy::lane_offset(lane);
+  const uint32_t svo = SCopy::lane_offset(lane);
+  const int skey = lane & 15;   // the key whose scales this lane copies
   auto kcopy = [&](int kbase, int buf) {
     return KCopy(p, p.k, g, kbase + 16 * w, smem_addr + buf * kKTile + 16 * w * 128);
   };
@@ -539,13 +580,13 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     return VCopy(p, p.v, g, kbase + 16 * w, smem_addr + kVOff + buf * 4 * kSegStride + 16 * w * 128);
   };
   auto scopy = [&](int kbase, int slot) {
-    return ScaleCopy(p, kbase + 16 * w, sk_addr + slot * kSkTile + w * 256);
+    return SCopy(p, kbase + 16 * w, sk_addr + slot * kSkTile + w * 256);
   };
   // whole-tile copies outside the pipelined loop
   auto copy_k_all = [&](int kbase, int buf, int slot) {
     const KCopy kc = kcopy(kbase, buf);
     static_for<0, KCopy::kInsts>([&](auto ic) { kc.template issue<decltype(ic)::value>(kvo); });
-    if constexpr (INT8K) scopy(kbase, slot).issue(svo);
+    if constexpr (INT8K) scopy(kbase, slot).issue(svo, skey);
   };
   auto copy_v_all = [&](int kbase, int buf) {
     const VCopy vc = vcopy(kbase, buf);
@@ -760,7 +801,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       const int kb1 = j + 1 < j1 ? kbase + kKt : p.kv_len;
       const KCopy kc = kcopy(kb2, j & 1);
       const VCopy vc = vcopy(kb1, (j + 1) & 1);
-      ScaleCopy scp;
+      SCopy scp;
       if constexpr (INT8K) scp = scopy(kb2, (j + 2) % 3);
       constexpr int kCopies = KCopy::kInsts + VCopy::kInsts + (INT8K ? 1 : 0);
       auto copy_issue = [&](auto ic) {
@@ -770,7 +811,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
         else if constexpr (I < KCopy::kInsts + VCopy::kInsts)
           vc.template issue<I - KCopy::kInsts>(vvo);
         else
-          scp.issue(svo);
+          scp.issue(svo, skey);
       };
       constexpr int kSlots = 2 * Q::kSteps;   // issue slots: the K steps of both halves
       // the copies whose slot (I * kSlots) / kCopies is SLOT
@@ -1075,7 +1116,9 @@ size_t workspace_bytes_for(int32_t q_len, int n_seg) {
 Launch plan_for(int32_t q_len, int32_t kv_len, bool paged, bool int8k) {
   (void)kv_len;
   Launch lc = shape_launch<kDefaultQB>(q_len, int8k);
-  if (int8k)
+  if (int8k && paged)
+    lc.name = kDefaultQB == 3 ? "int8k_paged_splitd_t32h6_kt64" : "int8k_paged_splitd_t64h2_kt64";
+  else if (int8k)
     lc.name = kDefaultQB == 3 ? "int8k_contiguous_t32h6_kt64" : "int8k_contiguous_t64h2_kt64";
   else if (paged)
     lc.name = kDefaultQB == 3 ? "bf16_paged_t32h6_kt64" : "bf16_paged_t64h2_kt64";
@@ -1094,7 +1137,6 @@ int prefill(const void* q, const void* k, const void* v, const int32_t* block_ta
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return GQA_ERR_NULL_ARG;
   const bool paged = block_table != nullptr;
   const bool int8k = k_scale != nullptr;
-  if (paged && int8k) return GQA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
     return GQA_ERR_MISALIGNED;
   if (paged && !aligned(block_table, 4)) return GQA_ERR_MISALIGNED;
@@ -1128,7 +1170,9 @@ int prefill(const void* q, const void* k, const void* v, const int32_t* block_ta
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(lc.workgroups * n_seg), block(lc.threads);
-  if (int8k)
+  if (int8k && paged)
+    hipLaunchKernelGGL((gqa_prefill_kernel<true, true, kDefaultQB>), grid, block, 0, s, p);
+  else if (int8k)
     hipLaunchKernelGGL((gqa_prefill_kernel<false, true, kDefaultQB>), grid, block, 0, s, p);
   else if (paged)
     hipLaunchKernelGGL((gqa_prefill_kernel<true, false, kDefaultQB>), grid, block, 0, s, p);
@@ -1156,7 +1200,7 @@ const char* gqa_status_string(int status) {
     case GQA_ERR_NULL_ARG: return "a required pointer is NULL";
     case GQA_ERR_BAD_LENGTH: return "invalid length (need 0 <= q_len <= kv_len <= GQA_MAX_LEN, rows >= 0, enough blocks)";
     case GQA_ERR_MISALIGNED: return "a tensor pointer is misaligned";
-    case GQA_ERR_UNSUPPORTED: return "unsupported combination (paged caches with INT8 keys)";
+    case GQA_ERR_UNSUPPORTED: return "unsupported combination of arguments";
     case GQA_ERR_HIP: return "HIP launch failed";
     case GQA_ERR_WORKSPACE: return "workspace missing or smaller than gqa_attn_prefill_workspace_size()";
     default: return "unknown status";
@@ -1166,7 +1210,6 @@ const char* gqa_status_string(int status) {
 int gqa_attn_prefill_plan(int32_t q_len, int32_t kv_len, int paged, int int8k, char* buf, size_t n) {
   if (buf == nullptr || n == 0) return GQA_ERR_NULL_ARG;
   int st = check_prefill_lengths(q_len, kv_len);
-  if (st == GQA_OK && paged && int8k) st = GQA_ERR_UNSUPPORTED;
   if (st != GQA_OK) {
     snprintf(buf, n, "error: %s", gqa_status_string(st));
     return st;
@@ -1180,7 +1223,7 @@ int gqa_attn_prefill_plan(int32_t q_len, int32_t kv_len, int paged, int int8k, c
 }
 
 size_t gqa_attn_prefill_workspace_size(int32_t q_len, int32_t kv_len, int paged, int int8k) {
-  if (check_prefill_lengths(q_len, kv_len) != GQA_OK || (paged && int8k)) return 0;
+  if (check_prefill_lengths(q_len, kv_len) != GQA_OK) return 0;
   const Launch lc = plan_for(q_len, kv_len, paged != 0, int8k != 0);
   return workspace_bytes_for(q_len, segments_for(q_len, kv_len, int8k != 0, lc.workgroups));
 }

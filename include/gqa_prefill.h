@@ -55,7 +55,7 @@ typedef enum gqa_status {
   GQA_ERR_BAD_LENGTH = 2,   /* q_len < 0, kv_len < q_len, a length above GQA_MAX_LEN,
                                rows < 0, or num_blocks too small for kv_len */
   GQA_ERR_MISALIGNED = 3,   /* a tensor pointer is not aligned as documented */
-  GQA_ERR_UNSUPPORTED = 4,  /* a combination this library refuses (paged + INT8 K) */
+  GQA_ERR_UNSUPPORTED = 4,  /* a combination this library refuses (none at present) */
   GQA_ERR_HIP = 5,          /* the HIP launch failed */
   GQA_ERR_WORKSPACE = 6     /* gqa_attn_prefill_ws: workspace NULL or too small */
 } gqa_status;
@@ -78,7 +78,10 @@ const char* gqa_status_string(int status);
  *        block_table != NULL: paged caches [num_blocks, 4, 16, 256], logical
  *        key t at cache[block_table[t / 16], :, t % 16, :].
  *        v is always bf16. k is bf16 when k_scale == NULL, and int8 codes when
- *        k_scale != NULL. 16-byte aligned.
+ *        k_scale != NULL: contiguous [kv_len, 4, 256], or, paged, the split-d
+ *        cache of "gfx936 DCU上实现INT8 QK MMAC" §3, [num_blocks, 4, 256/16, 16, 16]
+ *        with feature f of logical key t at
+ *        [block_table[t / 16], :, f / 16, t % 16, f % 16]. 16-byte aligned.
  * block_table  int32 [ceil(kv_len / 16)] or NULL; 4-byte aligned. Entries
  *        must lie in [0, num_blocks); an entry outside that range is clamped
  *        into it (the output is then wrong but no memory outside the caches is
@@ -86,7 +89,8 @@ const char* gqa_status_string(int status);
  * num_blocks   physical blocks in each paged cache; ignored when block_table
  *        is NULL; must be >= ceil(kv_len / 16) when it is not.
  * k_scale  float32 [kv_len, 4] (one scale per key token and KV head) or NULL;
- *        4-byte aligned. With INT8 keys each query row (token, head) is
+ *        with a block table, float32 [num_blocks, 4, 16], the scale of logical
+ *        key t at [block_table[t / 16], :, t % 16]. 4-byte aligned. With INT8 keys each query row (token, head) is
  *        quantised inside the call: sQ = max|q| / 127 in float32,
  *        Qq = round-half-even(q / sQ) (IEEE division), a zero row gives 0.
  * q_len, kv_len  0 <= q_len <= kv_len <= GQA_MAX_LEN. q_len == 0 is a no-op.
@@ -94,8 +98,8 @@ const char* gqa_status_string(int status);
  *        16-byte aligned; must not overlap q, k, v or the caches.
  * stream hipStream_t or NULL.
  *
- * Returns GQA_OK, GQA_ERR_NULL_ARG, GQA_ERR_BAD_LENGTH, GQA_ERR_MISALIGNED,
- * GQA_ERR_UNSUPPORTED (paged caches together with INT8 keys) or GQA_ERR_HIP.
+ * Returns GQA_OK, GQA_ERR_NULL_ARG, GQA_ERR_BAD_LENGTH, GQA_ERR_MISALIGNED or
+ * GQA_ERR_HIP.
  */
 int gqa_attn_prefill(const void* q, const void* k, const void* v,
                      const int32_t* block_table, int32_t num_blocks,

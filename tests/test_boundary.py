@@ -81,8 +81,11 @@ def test_null_pointers(which):
     assert call(**{which: None}) == NULL
 
 
-def test_paged_with_int8_keys_is_refused():
-    assert call(bt=16, nb=1, ks=16) == UNSUPPORTED
+def test_paged_int8_argument_errors():
+    # paged caches with INT8 keys are accepted; these argument errors return before any
+    # launch: a misaligned scale cache, and too few blocks for kv_len
+    assert call(bt=16, nb=1, ks=18) == MISALIGNED
+    assert call(bt=16, nb=0, ks=16, kv_len=8) == BADLEN
 
 
 @pytest.mark.parametrize("which", ["q", "k", "v", "out"])
@@ -120,8 +123,8 @@ def test_plan_describes_the_dispatch():
     assert "variant=bf16_paged" in binding.gqa_attn_prefill_plan(512, 32768, paged=True)
     assert "variant=int8k" in binding.gqa_attn_prefill_plan(3072, 16384, int8k=True)
     assert "workgroups=4" in binding.gqa_attn_prefill_plan(1, 1)
-    with pytest.raises(binding.GqaError):
-        binding.gqa_attn_prefill_plan(512, 32768, paged=True, int8k=True)
+    assert "variant=int8k_paged_splitd" in binding.gqa_attn_prefill_plan(512, 32768, paged=True,
+                                                                         int8k=True)
     with pytest.raises(binding.GqaError):
         binding.gqa_attn_prefill_plan(10, 5)
 
@@ -162,7 +165,8 @@ def test_workspace_size():
     assert binding.gqa_attn_prefill_workspace_size(32, 500) == 0
     # arguments the call would refuse
     assert binding.gqa_attn_prefill_workspace_size(10, 5) == 0
-    assert binding.gqa_attn_prefill_workspace_size(512, 32768, paged=True, int8k=True) == 0
+    assert binding.gqa_attn_prefill_workspace_size(512, 32768, paged=True, int8k=True) == \
+        SPLIT_512x32768
 
 
 def test_workspace_errors_return_before_launch():
