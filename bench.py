@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=3,
                     help="1 tiny, 2 4096x8192, 3 4096x32768 (default), 4 paged 512x32768, "
-                         "5 int8-k 3072x16384, 6 4096x16384, 7 paged int8-k 512x32768")
+                         "5 int8-k 3072x16384, 6 4096x16384, 7 paged int8-k 512x32768, "
+                         "8 decode 1x32768, 9 paged decode 1x32768")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="query rows of the workload the CPU oracle computes (all 24 heads)")
@@ -160,15 +161,27 @@ def main():
 
     flops = 4.0 * HQ * D * w.pairs_per_head
     tflops = flops / (ms * 1e-3) / 1e12
+    # algorithmic bytes: Q and out once, each K and V row once (int8 K: 1 byte a feature
+    # plus its scale), the block table
+    kv_rows = w.kv_len * HKV
+    alg_bytes = (2 * w.q_len * HQ * D * 2 + kv_rows * D * (1 if w.int8k else 2)
+                 + kv_rows * D * 2 + (kv_rows * 4 if w.int8k else 0)
+                 + (4 * ((w.kv_len + 15) // 16) if w.paged else 0))
+    if flops / alg_bytes < 315.0:
+        # below the ridge (2516.6 TFLOP/s / 8 TB/s): a decode-sized chunk is HBM-bound
+        gbs = alg_bytes / (ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                    "frac": round(gbs / 8000.0, 4), "traffic": load_traffic(w.name)}
     if w.int8k:
         # Q·K^T on int8 MFMA, P·V on bf16 MFMA: time at peak is the sum of both halves
         t_peak = (flops / 2) / (PEAK_INT8_TOPS * 1e12) + (flops / 2) / (PEAK_BF16_TFLOPS * 1e12)
         peak = flops / t_peak / 1e12
     else:
         peak = PEAK_BF16_TFLOPS
-    roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": round(peak, 1),
-                "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                "traffic": load_traffic(w.name)}
+    if flops / alg_bytes >= 315.0:
+        roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": round(peak, 1),
+                    "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                    "traffic": load_traffic(w.name)}
     rec = {
         "metric": METRIC,
         "value": round(tflops, 3),

@@ -962,36 +962,52 @@ __global__ __launch_bounds__(kThreads, 1) void gqa_prefill_kernel(const Params p
     run<PAGED, INT8K, QB, false>(p, smem);
 }
 
-// ---- merge of KV segments: one wave per output row (token, head), 4 features a lane ----
+// ---- merge of KV segments ----
 // Each segment took its exponentials against its own reference maximum m_s (log2
 // units) and left unnormalised O_s and the row sum l_s. With M the largest m_s,
 //   out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
 // the softmax over the whole history (a segment with l_s = 0 has no keys and weight 0).
 // Long histories are cut into segments the same way for decode attention and for
 // chunked prefill on the pages ("gfx936 DCU上实现INT8 QK MMAC" §4).
+//
+// Grid (output row = (token, head), 64-feature quarter of the row); the 4 waves of a
+// workgroup take every 4th segment, a lane one feature, so even a single decode token
+// (24 rows, up to 64 segments) keeps 384 waves loading independently; the waves' sums
+// meet in LDS. Loads are unconditional (the workspace holds n_seg full rows) and an
+// empty segment's contribution is dropped by a select, so whatever its O_s holds never
+// reaches the result.
 __global__ __launch_bounds__(256) void merge_segments_kernel(const float* ws_o, const float* ws_ml,
                                                              int n_seg, int64_t rows, uint8_t* out) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
+  const int64_t row = blockIdx.x;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int f = blockIdx.y * 64 + lane;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml);
   float mmax = -__builtin_inff();
-  for (int sg = 0; sg < n_seg; ++sg) {
+  for (int sg = lane; sg < n_seg; sg += 64) {
     const float2 v = ml[sg * rows + row];
-    if (v.y > 0.0f) mmax = fmaxf(mmax, v.x);
+    mmax = v.y > 0.0f ? fmaxf(mmax, v.x) : mmax;
   }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float lsum = 0.0f;
-  for (int sg = 0; sg < n_seg; ++sg) {
+  for (int x = 32; x >= 1; x >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, x));
+  float acc = 0.0f, lsum = 0.0f;
+#pragma unroll 4
+  for (int sg = wv; sg < n_seg; sg += 4) {
     const float2 v = ml[sg * rows + row];
-    if (v.y > 0.0f) {
-      const float wgt = __builtin_amdgcn_exp2f(v.x - mmax);
-      lsum += wgt * v.y;
-      acc += wgt * *reinterpret_cast<const f32x4*>(ws_o + ((size_t)(sg * rows + row)) * kD + 4 * lane);
-    }
+    const float o = ws_o[(size_t)(sg * rows + row) * kD + f];
+    const bool used = v.y > 0.0f;
+    const float wgt = __builtin_amdgcn_exp2f(v.x - mmax);
+    acc += used ? wgt * o : 0.0f;
+    lsum += used ? wgt * v.y : 0.0f;
   }
-  const f32x4 y = acc * (1.0f / lsum);
-  *reinterpret_cast<bf16x4*>(out + ((size_t)row * kD + 4 * lane) * 2) = __builtin_convertvector(y, bf16x4);
+  __shared__ float part[4][64];
+  __shared__ float lpart[4];
+  part[wv][lane] = acc;
+  if (lane == 0) lpart[wv] = lsum;
+  __syncthreads();
+  if (wv == 0) {
+    const float total = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    const float l = lpart[0] + lpart[1] + lpart[2] + lpart[3];
+    reinterpret_cast<__bf16*>(out)[(size_t)row * kD + f] = (__bf16)(total * (1.0f / l));
+  }
 }
 
 // ---- standalone row quantiser: one wave per 256-element row ----
@@ -1181,7 +1197,7 @@ int prefill(const void* q, const void* k, const void* v, const int32_t* block_ta
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
   if (n_seg > 1) {
     const int64_t rows = (int64_t)q_len * kHq;
-    hipLaunchKernelGGL(merge_segments_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+    hipLaunchKernelGGL(merge_segments_kernel, dim3((unsigned)rows, kD / 64), dim3(256), 0, s,
                        p.ws_o, p.ws_ml, n_seg, rows, p.out);
     if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
   }

@@ -64,6 +64,8 @@ WORKLOADS = {
     5: Workload("int8k_3072x16384", 3072, 16384, int8k=True, seed=5),
     6: Workload("chunk_4096x16384", 4096, 16384, seed=6),
     7: Workload("paged_int8k_512x32768", 512, 32768, paged=True, int8k=True, num_blocks=2048, seed=7),
+    8: Workload("decode_1x32768", 1, 32768, seed=8),
+    9: Workload("decode_paged_1x32768", 1, 32768, paged=True, num_blocks=2048, seed=9),
 }
 
 
