@@ -104,13 +104,19 @@ struct Params {
   float* ws_ml;            // n_seg > 1: (reference maximum, row sum) [n_seg, q_len, 24, 2]
 };
 
-// Workgroup shape for QB 16-column query blocks per wave.
+// Workgroup shape for QB 16-column query blocks per wave. QB = 3 and QB = 2 map a
+// column to a token (16-token runs) and a block to a query head. QB = 1 is the decode
+// shape: one token per wave, and column c of its single block is query head 6 g + c of
+// the GQA group (6 of the 16 columns are live). The pages make the same choice for
+// decode, where one new token cannot fill the 16 output rows of the matrix instruction
+// and the rows come from the group's query heads ("gfx936 DCU上实现INT8 QK MMAC" §5.1).
 template <int QB>
 struct Shape {
+  static constexpr bool kDecode = QB == 1;
   static constexpr int kTokenBlocks = (QB == 3) ? 2 : 4;            // 16-token runs per workgroup
-  static constexpr int kHeadGroups = kWaves / kTokenBlocks;         // QB-head groups per workgroup
-  static constexpr int kHeadsPerWg = QB * kHeadGroups;              // 6 or 2
-  static constexpr int kTokPerWg = 16 * kTokenBlocks;               // 32 or 64
+  static constexpr int kHeadGroups = kDecode ? 1 : kWaves / kTokenBlocks;   // QB-head groups
+  static constexpr int kHeadsPerWg = kDecode ? kGroup : QB * kHeadGroups;   // 6, 6 or 2
+  static constexpr int kTokPerWg = kDecode ? kWaves : 16 * kTokenBlocks;    // 4, 32 or 64
   static constexpr int kSplitsPerGroup = kGroup / kHeadsPerWg;      // 1 or 3 workgroups per (g, tokens)
 };
 
@@ -538,11 +544,13 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   const int tblk = p.n_tblk - 1 - rest / S::kSplitsPerGroup;
   const int t0 = tblk * S::kTokPerWg;
   const int off = p.kv_len - p.q_len;
-  const int head0 = kGroup * g + hsel * S::kHeadsPerWg + hw * QB;   // head of query block 0
+  const int head0 = S::kDecode ? kGroup * g + min(c, kGroup - 1)
+                                : kGroup * g + hsel * S::kHeadsPerWg + hw * QB;   // head of block 0
 
-  // query column (b, c) of this lane: token t0 + 16 tw + c, head head0 + b
-  const int tok = t0 + 16 * tw + c;
-  const bool tok_ok = tok < p.q_len;
+  // query column (b, c) of this lane: token t0 + 16 tw + c, head head0 + b; in the decode
+  // shape token t0 + w, head 6 g + c for c < 6 (head0 + b below always names the head)
+  const int tok = S::kDecode ? t0 + w : t0 + 16 * tw + c;
+  const bool tok_ok = tok < p.q_len && (!S::kDecode || c < kGroup);
   const int limit = off + tok;   // last visible key of this column
 
   const int last_tok = min(t0 + S::kTokPerWg, p.q_len);
@@ -1051,6 +1059,7 @@ int check_prefill_lengths(int32_t q_len, int32_t kv_len) {
 struct Launch {
   const char* name;
   int qb;
+  int tok_per_wg;
   int n_tblk;
   int workgroups;
   int threads;
@@ -1065,6 +1074,7 @@ Launch shape_launch(int32_t q_len, bool int8k) {
   const int n_tblk = (q_len + S::kTokPerWg - 1) / S::kTokPerWg;
   Launch lc;
   lc.qb = QB;
+  lc.tok_per_wg = S::kTokPerWg;
   lc.n_tblk = n_tblk;
   lc.workgroups = n_tblk * kHkv * S::kSplitsPerGroup;
   lc.threads = kThreads;
@@ -1082,9 +1092,8 @@ constexpr int kMinSegTiles = 8;  // shortest KV segment (512 keys)
 // two tile times of prologue and epilogue; and a split launch moves n_seg partial rows
 // of 1 KiB + 8 B per output row through memory twice (written, then read by the merge)
 // at about 5 TB/s, against the ~2.4 us a workgroup spends on one tile.
-double plan_cost(int32_t q_len, int32_t kv_len, int n_tblk, int n_seg) {
+double plan_cost(int32_t q_len, int32_t kv_len, int tok, int n_tblk, int n_seg) {
   constexpr double kWgTiles = 2.0;
-  const int tok = Shape<GQA_DEFAULT_QB>::kTokPerWg;
   const int64_t pieces = (int64_t)kHkv * n_tblk * n_seg;
   double t = 0.0;
   for (int64_t first = 0; first < pieces; first += kCUs) {
@@ -1102,18 +1111,18 @@ double plan_cost(int32_t q_len, int32_t kv_len, int n_tblk, int n_seg) {
 // and splitting it further was measured to gain nothing). A smaller grid takes the
 // count with the lowest plan_cost among those that keep every segment at least
 // kMinSegTiles long in the shortest (first) token block.
-int segments_for(int32_t q_len, int32_t kv_len, bool int8k, int unsplit_workgroups) {
-  (void)int8k;
+int segments_for(int32_t q_len, int32_t kv_len, const Launch& lc) {
+  const int unsplit_workgroups = lc.workgroups;
   if (q_len == 0 || unsplit_workgroups >= kCUs) return 1;
-  const int tok = Shape<GQA_DEFAULT_QB>::kTokPerWg;
-  const int n_tblk = (q_len + tok - 1) / tok;
+  const int tok = lc.tok_per_wg;
+  const int n_tblk = lc.n_tblk;
   const int64_t t_min = ((int64_t)kv_len - q_len + std::min(q_len, tok) + kKt - 1) / kKt;
   int best = 1;
-  double best_cost = plan_cost(q_len, kv_len, n_tblk, 1);
+  double best_cost = plan_cost(q_len, kv_len, tok, n_tblk, 1);
   static const int kCandidates[] = {2, 3, 4, 5, 6, 8, 10, 12, 16, 24, 32, 48, 64};
   for (int n : kCandidates) {
     if (t_min / n < kMinSegTiles) break;
-    const double c = plan_cost(q_len, kv_len, n_tblk, n);
+    const double c = plan_cost(q_len, kv_len, tok, n_tblk, n);
     if (c < 0.97 * best_cost) {   // split only for a clear gain
       best = n;
       best_cost = c;
@@ -1127,19 +1136,25 @@ size_t workspace_bytes_for(int32_t q_len, int n_seg) {
   return (size_t)n_seg * q_len * kHq * (kD + 2) * sizeof(float);
 }
 
-// Dispatch rule (the analogue of the pages' q_len/kv_len-gated variant choice): one
-// kernel family; the query-block count per wave is the only shape parameter.
+// Chunks of at most this many query tokens run the decode shape (4 tokens x 6 heads
+// per workgroup, a token per wave) instead of 32 tokens x 6 heads.
+constexpr int kDecodeMaxQ = 4;
+
+// Dispatch rule (the analogue of the pages' q_len/kv_len-gated variant choice, and of
+// their separate decode and prefill row mappings): one kernel family; the shape of the
+// query block is the only parameter.
 Launch plan_for(int32_t q_len, int32_t kv_len, bool paged, bool int8k) {
   (void)kv_len;
-  Launch lc = shape_launch<kDefaultQB>(q_len, int8k);
-  if (int8k && paged)
-    lc.name = kDefaultQB == 3 ? "int8k_paged_splitd_t32h6_kt64" : "int8k_paged_splitd_t64h2_kt64";
-  else if (int8k)
-    lc.name = kDefaultQB == 3 ? "int8k_contiguous_t32h6_kt64" : "int8k_contiguous_t64h2_kt64";
-  else if (paged)
-    lc.name = kDefaultQB == 3 ? "bf16_paged_t32h6_kt64" : "bf16_paged_t64h2_kt64";
-  else
-    lc.name = kDefaultQB == 3 ? "bf16_contiguous_t32h6_kt64" : "bf16_contiguous_t64h2_kt64";
+  const bool dec = q_len <= kDecodeMaxQ;
+  Launch lc = dec ? shape_launch<1>(q_len, int8k) : shape_launch<kDefaultQB>(q_len, int8k);
+  static const char* const kNames[4][3] = {
+      // decode, 32 tokens x 6 heads, 64 tokens x 2 heads
+      {"bf16_contiguous_decode_t4h6_kt64", "bf16_contiguous_t32h6_kt64", "bf16_contiguous_t64h2_kt64"},
+      {"bf16_paged_decode_t4h6_kt64", "bf16_paged_t32h6_kt64", "bf16_paged_t64h2_kt64"},
+      {"int8k_contiguous_decode_t4h6_kt64", "int8k_contiguous_t32h6_kt64", "int8k_contiguous_t64h2_kt64"},
+      {"int8k_paged_splitd_decode_t4h6_kt64", "int8k_paged_splitd_t32h6_kt64",
+       "int8k_paged_splitd_t64h2_kt64"}};
+  lc.name = kNames[(int8k ? 2 : 0) + (paged ? 1 : 0)][dec ? 0 : (lc.qb == 3 ? 1 : 2)];
   return lc;
 }
 
@@ -1162,7 +1177,7 @@ int prefill(const void* q, const void* k, const void* v, const int32_t* block_ta
     if (num_blocks < need || num_blocks <= 0) return GQA_ERR_BAD_LENGTH;
   }
   const Launch lc = plan_for(q_len, kv_len, paged, int8k);
-  const int n_seg = allow_split ? segments_for(q_len, kv_len, int8k, lc.workgroups) : 1;
+  const int n_seg = allow_split ? segments_for(q_len, kv_len, lc) : 1;
   const size_t ws_need = workspace_bytes_for(q_len, n_seg);
   if (n_seg > 1) {
     if (workspace == nullptr || workspace_bytes < ws_need) return GQA_ERR_WORKSPACE;
@@ -1186,14 +1201,21 @@ int prefill(const void* q, const void* k, const void* v, const int32_t* block_ta
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(lc.workgroups * n_seg), block(lc.threads);
-  if (int8k && paged)
-    hipLaunchKernelGGL((gqa_prefill_kernel<true, true, kDefaultQB>), grid, block, 0, s, p);
-  else if (int8k)
-    hipLaunchKernelGGL((gqa_prefill_kernel<false, true, kDefaultQB>), grid, block, 0, s, p);
-  else if (paged)
-    hipLaunchKernelGGL((gqa_prefill_kernel<true, false, kDefaultQB>), grid, block, 0, s, p);
+  auto launch = [&](auto qb_c) {
+    constexpr int QB = decltype(qb_c)::value;
+    if (int8k && paged)
+      hipLaunchKernelGGL((gqa_prefill_kernel<true, true, QB>), grid, block, 0, s, p);
+    else if (int8k)
+      hipLaunchKernelGGL((gqa_prefill_kernel<false, true, QB>), grid, block, 0, s, p);
+    else if (paged)
+      hipLaunchKernelGGL((gqa_prefill_kernel<true, false, QB>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((gqa_prefill_kernel<false, false, QB>), grid, block, 0, s, p);
+  };
+  if (lc.qb == 1)
+    launch(std::integral_constant<int, 1>{});
   else
-    hipLaunchKernelGGL((gqa_prefill_kernel<false, false, kDefaultQB>), grid, block, 0, s, p);
+    launch(std::integral_constant<int, kDefaultQB>{});
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
   if (n_seg > 1) {
     const int64_t rows = (int64_t)q_len * kHq;
@@ -1231,7 +1253,7 @@ int gqa_attn_prefill_plan(int32_t q_len, int32_t kv_len, int paged, int int8k, c
     return st;
   }
   const Launch lc = plan_for(q_len, kv_len, paged != 0, int8k != 0);
-  const int n_seg = segments_for(q_len, kv_len, int8k != 0, lc.workgroups);
+  const int n_seg = segments_for(q_len, kv_len, lc);
   snprintf(buf, n, "variant=%s workgroups=%d threads=%d lds_bytes=%d segments=%d workspace_bytes=%zu",
            lc.name, lc.workgroups * n_seg, lc.threads, lc.lds_bytes, n_seg,
            workspace_bytes_for(q_len, n_seg));
@@ -1241,7 +1263,7 @@ int gqa_attn_prefill_plan(int32_t q_len, int32_t kv_len, int paged, int int8k, c
 size_t gqa_attn_prefill_workspace_size(int32_t q_len, int32_t kv_len, int paged, int int8k) {
   if (check_prefill_lengths(q_len, kv_len) != GQA_OK) return 0;
   const Launch lc = plan_for(q_len, kv_len, paged != 0, int8k != 0);
-  return workspace_bytes_for(q_len, segments_for(q_len, kv_len, int8k != 0, lc.workgroups));
+  return workspace_bytes_for(q_len, segments_for(q_len, kv_len, lc));
 }
 
 int gqa_attn_prefill(const void* q, const void* k, const void* v, const int32_t* block_table,
