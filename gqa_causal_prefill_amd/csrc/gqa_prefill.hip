@@ -691,11 +691,66 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     qk_pair<INT8K, QB, 0>(kbuf, kb_even, kb_odd, qf, sacc, [](auto) {});
     qk_pair<INT8K, QB, 2>(kbuf, kb_even, kb_odd, qf, sacc, [](auto) {});
   };
+  // INT8 keys: sacc holds int32 dot products until scale_unit turns them, in place, into
+  // float scores in log2 units (their bit patterns): y = float(S) * (sK * sQ * log2(e)/16),
+  // or, inside the tile loop where the pass's reference maximum m is fixed, the exponent
+  // y - m itself as one fused multiply-add. Both forms are written out explicitly (no
+  // contraction left to the compiler), so every build rounds every score the same way.
+  // The scales of keys 16 kb + 4 L .. + 3 for KV head g come from one 16-byte LDS read
+  // per 16-key block kb.
+  auto sk_read = [&](uint32_t sk_slot, u32x4 (&sr)[4]) {
+    const uint32_t a = sk_slot + g * 64 + 16 * L;
+    sr[0] = lds_read_b128<0>(a);
+    sr[1] = lds_read_b128<256>(a);
+    sr[2] = lds_read_b128<512>(a);
+    sr[3] = lds_read_b128<768>(a);
+  };
+  auto scale_unit = [&](auto kb_c, auto b_c, const u32x4 (&sr)[4], auto minus_m_c) {
+#pragma clang fp contract(off)
+    constexpr int kb = decltype(kb_c)::value, b = decltype(b_c)::value;
+    const f32x4 skv = __builtin_bit_cast(f32x4, sr[kb]);
+    f32x4 y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (decltype(minus_m_c)::value)
+        y[r] = __builtin_fmaf((float)sacc[b][kb][r], skv[r] * qs[b], -m[b]);
+      else
+        y[r] = (float)sacc[b][kb][r] * (skv[r] * qs[b]);
+    }
+    sacc[b][kb] = __builtin_bit_cast(Acc, y);
+  };
+  // the whole tile at once (outside the pipelined loop)
+  auto scale_tile = [&](uint32_t sk_slot) {
+    if constexpr (INT8K) {
+      u32x4 sr[4];
+      sk_read(sk_slot, sr);
+      lds_wait4<0>(sr[0], sr[1], sr[2], sr[3]);
+      static_for<0, 4 * QB>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        scale_unit(std::integral_constant<int, u / QB>{}, std::integral_constant<int, u % QB>{}, sr,
+                   std::false_type{});
+      });
+    }
+  };
+  // the first tile of a pass: y -> y - m once m is known
+  auto shift_tile = [&]() {
+    if constexpr (INT8K) {
+#pragma clang fp contract(off)
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          f32x4 y = __builtin_bit_cast(f32x4, sacc[b][kb]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[r] = y[r] - m[b];
+          sacc[b][kb] = __builtin_bit_cast(Acc, y);
+        }
+    }
+  };
   // scores of key blocks 2h, 2h + 1 (keys kbase + 32 h .. + 31) from sacc, in log2 units
   // once multiplied by scale[b] (bf16: raw dot products; INT8 keys: already scaled),
   // causal mask applied. sc[b][e]: e = 0..3 keys 32 h + 4 L + e, e = 4..7 keys 32 h + 16 + 4 L + e - 4
-  auto half_scores = [&](auto mask_c, uint32_t sk_slot, int kbase, int h, float (&sc)[QB][8],
-                         float (&scale)[QB]) {
+  auto half_scores = [&](auto mask_c, int kbase, int h, float (&sc)[QB][8], float (&scale)[QB]) {
     constexpr bool kMask = decltype(mask_c)::value;
     if constexpr (!INT8K) {
 #pragma unroll
@@ -706,26 +761,17 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) sc[b][4 * kk + r] = sacc[b][2 * h + kk][r];
       }
-    } else {
-      // The score is rounded once as float(S) * (sK * sQ * log2(e)/16) and only then
-      // offset by the maximum: no fusing of this product into a later add, so every
-      // build (whatever it schedules around this code) rounds every score the same way.
-#pragma clang fp contract(off)
-      // scales of keys 16 (2 h + kk) + 4 L .. + 3 for KV head g
-      u32x4 sr[2];
-      const uint32_t a = sk_slot + 2 * h * 256 + g * 64 + 16 * L;
-      sr[0] = lds_read_b128<0>(a);
-      sr[1] = lds_read_b128<256>(a);
-      lds_wait2<0>(sr[0], sr[1]);
+    } else {   // already scaled: y for the maxima of a first tile, else y - m, which
+               // the softmax takes as the exponent (bit-cast whole vectors: a cast of
+               // one vector element by reference would not name that element)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const f32x4 skv = __builtin_bit_cast(f32x4, sr[kk]);
+      for (int b = 0; b < QB; ++b)
 #pragma unroll
-        for (int b = 0; b < QB; ++b)
+        for (int kk = 0; kk < 2; ++kk) {
+          const f32x4 sf = __builtin_bit_cast(f32x4, sacc[b][2 * h + kk]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            sc[b][4 * kk + r] = (float)sacc[b][2 * h + kk][r] * (skv[r] * qs[b]);
-      }
+          for (int r = 0; r < 4; ++r) sc[b][4 * kk + r] = sf[r];
+        }
 #pragma unroll
       for (int b = 0; b < QB; ++b) scale[b] = 1.0f;
     }
@@ -750,10 +796,10 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     return mx;
   };
   // column maxima of the whole tile in sacc (reduced over the 4 lanes of a column)
-  auto tile_max = [&](uint32_t sk_slot, int kbase, float (&mx)[QB]) {
+  auto tile_max = [&](int kbase, float (&mx)[QB]) {
     float sc0[QB][8], sc1[QB][8], scale[QB];
-    half_scores(std::true_type{}, sk_slot, kbase, 0, sc0, scale);
-    half_scores(std::true_type{}, sk_slot, kbase, 1, sc1, scale);
+    half_scores(std::true_type{}, kbase, 0, sc0, scale);
+    half_scores(std::true_type{}, kbase, 1, sc1, scale);
 #pragma unroll
     for (int b = 0; b < QB; ++b)
       mx[b] = xor32_max(xor16_max(fmaxf(lane_max(sc0, b), lane_max(sc1, b)))) * scale[b];
@@ -785,7 +831,9 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     wait_vm_all();
     __syncthreads();
     qk_tile(smem_addr + (j0 & 1) * kKTile);   // S(j0)
-    if (pass == 0) tile_max(sk_addr + (j0 % 3) * kSkTile, j0 * kKt, m);
+    scale_tile(sk_addr + (j0 % 3) * kSkTile);
+    if (pass == 0) tile_max(j0 * kKt, m);
+    shift_tile();
     __syncthreads();   // every wave is done with K(j0) before K(j0+2) overwrites it
 
     // Tiles that end at or before the workgroup's first query need no causal mask; the
@@ -839,7 +887,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       auto half = [&](auto hc) {
         constexpr int H = decltype(hc)::value;
         float sc[QB][8], scale[QB];
-        half_scores(mask_c, sk_addr + (j % 3) * kSkTile, kbase, H, sc, scale);
+        half_scores(mask_c, kbase, H, sc, scale);
 #pragma unroll
         for (int b = 0; b < QB; ++b) sacc[b][2 * H] = sacc[b][2 * H + 1] = Acc{0, 0, 0, 0};
         // P for query block b after K step ((b + 1) * steps) / QB - 1 of this half
@@ -853,7 +901,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
               f32x8 pv;
 #pragma unroll
               for (int e = 0; e < 8; ++e)
-                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][e], scale[b], nm));
+                pv[e] = __builtin_amdgcn_exp2f(INT8K ? sc[b][e] : __builtin_fmaf(sc[b][e], scale[b], nm));
               ph[b][H] = __builtin_convertvector(pv, bf16x8);
               if constexpr (SPLIT)
                 pl[b][H] = __builtin_convertvector(pv - __builtin_convertvector(ph[b][H], f32x8), bf16x8);
@@ -865,8 +913,12 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       half(std::integral_constant<int, 0>{});
       half(std::integral_constant<int, 1>{});
 
-      // ---- O^T += V^T(j) · P^T(j) ----
+      // ---- O^T += V^T(j) · P^T(j); INT8 keys: S(j+1) is scaled between the steps, where
+      // the vector ALU has room (the Q·K^T halves above are short on it: half as many
+      // MFMAs as with bf16 keys for the same softmax work) ----
       {
+        u32x4 sr[4];   // scales of tile j + 1 (copied two iterations ago)
+        if constexpr (INT8K) sk_read(sk_addr + ((j + 1) % 3) * kSkTile, sr);
         uint32_t vbase[4];
         const uint32_t v0 = lds_addr(vcur);
 #pragma unroll
@@ -875,7 +927,19 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
         static_for<0, kVtDepth>([&](auto nc) {   // the first kVtDepth steps' reads
           vt_issue_step<decltype(nc)::value>(vf[decltype(nc)::value], vbase);
         });
-        PvStep<0, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc, [](auto) {});
+        PvStep<0, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc, [&](auto nc) {
+          if constexpr (INT8K) {
+            constexpr int N = decltype(nc)::value;
+            // at step 1 only the 2 kVtDepth reads of steps 1 .. kVtDepth are younger
+            // than the scale reads: the wait costs nothing and marks them valid
+            if constexpr (N == 1) lds_wait4<2 * kVtDepth>(sr[0], sr[1], sr[2], sr[3]);
+            if constexpr (N >= 2 && N % 2 == 0 && (N - 2) / 2 < 4 * QB) {
+              constexpr int u = (N - 2) / 2;
+              scale_unit(std::integral_constant<int, u / QB>{}, std::integral_constant<int, u % QB>{}, sr,
+                         std::true_type{});
+            }
+          }
+        });
       }
 
       // Flags are double-buffered by tile parity: the write for tile j + 2 happens only
@@ -917,8 +981,9 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       wait_vm_all();
       __syncthreads();
       qk_tile(smem_addr);
+      scale_tile(sk_addr);
       float mx[QB];
-      tile_max(sk_addr, t * kKt, mx);
+      tile_max(t * kKt, mx);
 #pragma unroll
       for (int b = 0; b < QB; ++b) m[b] = fmaxf(m[b], mx[b]);
       __syncthreads();
