@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     gqa_abi_version,
     gqa_attn_prefill,
     gqa_attn_prefill_plan,
+    gqa_attn_prefill_qint8,
     gqa_attn_prefill_workspace_size,
     gqa_attn_prefill_ws,
     gqa_quantize_rows_int8,

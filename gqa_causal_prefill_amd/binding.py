@@ -63,6 +63,9 @@ def library() -> ctypes.CDLL:
         lib.gqa_attn_prefill_ws.restype = ctypes.c_int
         lib.gqa_attn_prefill_ws.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, vp,
                                             ctypes.c_size_t, vp]
+        lib.gqa_attn_prefill_qint8.restype = ctypes.c_int
+        lib.gqa_attn_prefill_qint8.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, vp,
+                                               ctypes.c_size_t, vp]
         lib.gqa_attn_prefill_workspace_size.restype = ctypes.c_size_t
         lib.gqa_attn_prefill_workspace_size.argtypes = [i32, i32, ctypes.c_int, ctypes.c_int]
         lib.gqa_quantize_rows_int8.restype = ctypes.c_int
@@ -117,7 +120,8 @@ def _expect(t, name, dtype, shape, device):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out):
+def _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out,
+                  q_dtype=torch.bfloat16):
     """Checks dtypes, shapes, contiguity and device; returns the C arguments and out."""
     dev = q.device
     if dev.type != "cuda":
@@ -137,7 +141,7 @@ def _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out)
         kv_len = k.shape[0] if kv_len is None else kv_len
         nb = 0
         k_shape = v_shape = (kv_len, NUM_KV_HEADS, HEAD_DIM)
-    _expect(q, "q", torch.bfloat16, (q_len, NUM_Q_HEADS, HEAD_DIM), dev)
+    _expect(q, "q", q_dtype, (q_len, NUM_Q_HEADS, HEAD_DIM), dev)
     _expect(k, "k", torch.int8 if k_scale is not None else torch.bfloat16, k_shape, dev)
     _expect(v, "v", torch.bfloat16, v_shape, dev)
     if k_scale is not None:
@@ -182,21 +186,49 @@ def gqa_attn_prefill_ws(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     gqa_attn_prefill_ws in include/gqa_prefill.h). `workspace` is a device tensor of
     at least gqa_attn_prefill_workspace_size() bytes; when it is None and the call
     splits, one is allocated through torch for this call."""
-    args, out, (ql, kl, paged, int8k) = _prefill_args(q, k, v, block_table, num_blocks,
-                                                      k_scale, q_len, kv_len, out)
-    if workspace is None:
-        need = gqa_attn_prefill_workspace_size(ql, kl, paged, int8k)
-        if need > 0:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    if workspace is not None:
-        if workspace.device != q.device or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous tensor on " + str(q.device))
-        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
-    else:
-        ws_ptr, ws_bytes = None, 0
+    args, out, lens = _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len,
+                                    out)
+    ws_ptr, ws_bytes = _workspace_args(workspace, lens, q.device)
     st = library().gqa_attn_prefill_ws(*args, ws_ptr, ws_bytes, _stream_handle(q, stream))
     if st != GQA_OK:
         raise GqaError(st, "gqa_attn_prefill_ws")
+    return out
+
+
+def _workspace_args(workspace, lens, dev):
+    """(pointer, bytes) of the caller's workspace, or of one allocated through torch
+    for this call when it is None and the call splits."""
+    if workspace is None:
+        need = gqa_attn_prefill_workspace_size(*lens)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is None:
+        return None, 0
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on " + str(dev))
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def gqa_attn_prefill_qint8(q_codes: torch.Tensor, q_scale: torch.Tensor, k: torch.Tensor,
+                           v: torch.Tensor, block_table: torch.Tensor | None = None,
+                           num_blocks: int | None = None, k_scale: torch.Tensor | None = None,
+                           q_len: int | None = None, kv_len: int | None = None,
+                           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                           stream=None) -> torch.Tensor:
+    """INT8-key attention with Q quantised beforehand (see gqa_attn_prefill_qint8 in
+    include/gqa_prefill.h): q_codes int8 [q_len, 24, 256] and q_scale float32
+    [q_len, 24], as gqa_quantize_rows_int8 returns them; k_scale is required; the
+    other arguments are those of gqa_attn_prefill_ws."""
+    if k_scale is None:
+        raise ValueError("gqa_attn_prefill_qint8 takes INT8 keys: k_scale is required")
+    args, out, lens = _prefill_args(q_codes, k, v, block_table, num_blocks, k_scale, q_len,
+                                    kv_len, out, q_dtype=torch.int8)
+    _expect(q_scale, "q_scale", torch.float32, (lens[0], NUM_Q_HEADS), q_codes.device)
+    ws_ptr, ws_bytes = _workspace_args(workspace, lens, q_codes.device)
+    st = library().gqa_attn_prefill_qint8(args[0], _ptr(q_scale), *args[1:], ws_ptr, ws_bytes,
+                                          _stream_handle(q_codes, stream))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_attn_prefill_qint8")
     return out
 
 

@@ -89,7 +89,8 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct Params {
-  const uint8_t* q;        // bf16 [q_len, 24, 256]
+  const uint8_t* q;        // bf16 [q_len, 24, 256], or int8 codes of Q when qsc is set
+  const float* qsc;        // INT8 keys, Q quantised beforehand: sQ [q_len, 24]; else null
   const uint8_t* k;        // bf16 or int8, contiguous or paged
   const uint8_t* v;        // bf16, contiguous or paged
   const int32_t* bt;       // block table or null
@@ -620,6 +621,18 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
                            : make_uint4(0, 0, 0, 0);
         qf[b][s] = __builtin_bit_cast(bf16x8, raw);
       }
+    } else if (p.qsc != nullptr) {
+      // Q quantised beforehand: the fragment is bytes 64 s + 16 L .. + 15 of the row's
+      // codes, the same one the quantising form below packs
+      const uint8_t* crow = p.q + ((size_t)tok * kHq + head0 + b) * kD;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 raw = tok_ok ? *reinterpret_cast<const uint4*>(crow + 64 * s + 16 * L)
+                                 : make_uint4(0, 0, 0, 0);
+        qf[b][s] = __builtin_bit_cast(i32x4, raw);
+      }
+      const float sq = tok_ok ? p.qsc[(size_t)tok * kHq + head0 + b] : 0.0f;
+      qs[b] = sq * kLog2eOver16;
     } else {
       // each lane holds features 64 s + 16 L .. +15 (s = 0..3) of its query row;
       // the four lanes L = 0..3 of column c hold the whole row
@@ -1223,10 +1236,12 @@ Launch plan_for(int32_t q_len, int32_t kv_len, bool paged, bool int8k) {
   return lc;
 }
 
-// Shared by both entry points; `allow_split` is false for the call without a workspace.
-int prefill(const void* q, const void* k, const void* v, const int32_t* block_table,
-            int32_t num_blocks, const float* k_scale, int32_t q_len, int32_t kv_len, void* out,
-            void* workspace, size_t workspace_bytes, bool allow_split, void* stream) {
+// Shared by the entry points; `allow_split` is false for the call without a workspace,
+// `q_scale` is set (and q holds int8 codes) only for the call with Q quantised beforehand.
+int prefill(const void* q, const float* q_scale, const void* k, const void* v,
+            const int32_t* block_table, int32_t num_blocks, const float* k_scale, int32_t q_len,
+            int32_t kv_len, void* out, void* workspace, size_t workspace_bytes, bool allow_split,
+            void* stream) {
   int st = check_prefill_lengths(q_len, kv_len);
   if (st != GQA_OK) return st;
   if (q_len == 0) return GQA_OK;
@@ -1237,6 +1252,7 @@ int prefill(const void* q, const void* k, const void* v, const int32_t* block_ta
     return GQA_ERR_MISALIGNED;
   if (paged && !aligned(block_table, 4)) return GQA_ERR_MISALIGNED;
   if (int8k && !aligned(k_scale, 4)) return GQA_ERR_MISALIGNED;
+  if (q_scale != nullptr && !aligned(q_scale, 4)) return GQA_ERR_MISALIGNED;
   if (paged) {
     const int64_t need = ((int64_t)kv_len + kBs - 1) / kBs;
     if (num_blocks < need || num_blocks <= 0) return GQA_ERR_BAD_LENGTH;
@@ -1251,6 +1267,7 @@ int prefill(const void* q, const void* k, const void* v, const int32_t* block_ta
 
   Params p;
   p.q = static_cast<const uint8_t*>(q);
+  p.qsc = q_scale;
   p.k = static_cast<const uint8_t*>(k);
   p.v = static_cast<const uint8_t*>(v);
   p.bt = block_table;
@@ -1334,15 +1351,26 @@ size_t gqa_attn_prefill_workspace_size(int32_t q_len, int32_t kv_len, int paged,
 int gqa_attn_prefill(const void* q, const void* k, const void* v, const int32_t* block_table,
                      int32_t num_blocks, const float* k_scale, int32_t q_len, int32_t kv_len,
                      void* out, void* stream) {
-  return prefill(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out, nullptr, 0, false,
-                 stream);
+  return prefill(q, nullptr, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out, nullptr, 0,
+                 false, stream);
 }
 
 int gqa_attn_prefill_ws(const void* q, const void* k, const void* v, const int32_t* block_table,
                         int32_t num_blocks, const float* k_scale, int32_t q_len, int32_t kv_len,
                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
-  return prefill(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out, workspace,
+  return prefill(q, nullptr, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out, workspace,
                  workspace_bytes, true, stream);
+}
+
+int gqa_attn_prefill_qint8(const void* q_codes, const float* q_scale, const void* k, const void* v,
+                           const int32_t* block_table, int32_t num_blocks, const float* k_scale,
+                           int32_t q_len, int32_t kv_len, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const int st = check_prefill_lengths(q_len, kv_len);
+  if (st != GQA_OK || q_len == 0) return st;
+  if (q_scale == nullptr || k_scale == nullptr) return GQA_ERR_NULL_ARG;
+  return prefill(q_codes, q_scale, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out,
+                 workspace, workspace_bytes, true, stream);
 }
 
 int gqa_quantize_rows_int8(const void* x, int64_t rows, void* xq, float* scale, void* stream) {

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define GQA_ABI_VERSION 2
+#define GQA_ABI_VERSION 3
 #define GQA_NUM_Q_HEADS 24
 #define GQA_NUM_KV_HEADS 4
 #define GQA_HEAD_DIM 256
@@ -145,6 +145,31 @@ int gqa_attn_prefill_ws(const void* q, const void* k, const void* v,
                         const float* k_scale, int32_t q_len, int32_t kv_len,
                         void* out, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/*
+ * gqa_attn_prefill_qint8 - the INT8-key call with Q quantised beforehand.
+ *
+ * "gfx936 DCU上实现INT8 QK MMAC" §4 quantises each query row once, before the
+ * attention (in the producer that writes Q), so that the KV segments of a long history
+ * share one set of codes instead of each reducing and rounding the row again. This
+ * entry point takes those codes: with q_codes and q_scale written by
+ * gqa_quantize_rows_int8 from a bf16 Q (rows = q_len * 24), the result is bit for bit
+ * that of gqa_attn_prefill_ws on that Q with the same keys and values.
+ *
+ * q_codes  int8 [q_len, 24, 256]: Qq of each query row (token, head); 16-byte aligned.
+ * q_scale  float32 [q_len, 24]: sQ of each row, score = int32(Qq·Kqᵀ)·sQ·sK/16;
+ *          4-byte aligned. Required.
+ * k_scale  required (INT8 keys); k, v, block_table, num_blocks, k_scale, q_len, kv_len,
+ *          out, workspace, workspace_bytes and stream as for gqa_attn_prefill_ws, whose
+ *          workspace size (int8k = 1) applies.
+ *
+ * Returns the codes of gqa_attn_prefill_ws; GQA_ERR_NULL_ARG also when q_scale or
+ * k_scale is NULL (for q_len > 0).
+ */
+int gqa_attn_prefill_qint8(const void* q_codes, const float* q_scale, const void* k,
+                           const void* v, const int32_t* block_table, int32_t num_blocks,
+                           const float* k_scale, int32_t q_len, int32_t kv_len, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gqa_quantize_rows_int8 - the per-row INT8 quantiser of "gfx936 DCU上实现INT8 QK

@@ -38,6 +38,7 @@ from .prefill import (  # noqa: F401
     SCALE,
     BLOCK_SIZE,
     attention,
+    attention_int8,
     attention_int8k,
     causal_limit,
     gather_paged,

@@ -251,11 +251,23 @@ def attention_int8k(q, kq, k_scale, v, rows=None, heads=None, chunk=256,
     k_scale: float32 [kv_len, 4] (one scale per key token and KV head);
     v: [kv_len, 4, 256]. Each query row (token, head) is quantised once with
     ``quantize_rows_int8`` [INT8 QK §4: the query is quantised once, before the
-    attention]; scores come from ``score_matrix_int8k``; the rest is as in
-    ``attention``.
+    attention], then ``attention_int8`` runs on the codes.
     """
     qq, sq = quantize_rows_int8(q)
-    qq = qq.astype(np.float64)
+    return attention_int8(qq, sq, kq, k_scale, v, rows, heads, chunk, return_weights)
+
+
+def attention_int8(qq, q_scale, kq, k_scale, v, rows=None, heads=None, chunk=256,
+                   return_weights=False):
+    """Causal GQA prefill attention on INT8 query and key codes [INT8 QK §1, §4].
+
+    The form the pages arrive at in [INT8 QK §4], where the producer of Q has
+    already quantised each query row: qq int8 [q_len, 24, 256] with q_scale
+    float32 [q_len, 24], kq int8 [kv_len, 4, 256] with k_scale [kv_len, 4], and
+    v [kv_len, 4, 256]. Scores come from ``score_matrix_int8k``; the rest is as
+    in ``attention``. The codes need not come from ``quantize_rows_int8``.
+    """
+    qq = _as_f64(qq)
     kqf = _as_f64(kq)
     ks = _as_f64(k_scale)
     v = _as_f64(v)
@@ -264,7 +276,9 @@ def attention_int8k(q, kq, k_scale, v, rows=None, heads=None, chunk=256,
         raise ValueError("bad shapes for the INT8-K oracle")
     if v.shape != (kv_len, HKV, D) or q_len > kv_len:
         raise ValueError("bad shapes for the INT8-K oracle")
-    sq64 = sq.astype(np.float64)
+    sq64 = _as_f64(q_scale)
+    if sq64.shape != (q_len, HQ):
+        raise ValueError("bad shapes for the INT8-K oracle")
 
     def scores(h, idx, nk):
         return score_matrix_int8k(qq, sq64, kqf, ks, h, idx, nk)

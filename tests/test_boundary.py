@@ -36,8 +36,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"gqa_attn_prefill", "gqa_attn_prefill_ws", "gqa_attn_prefill_workspace_size",
-            "gqa_quantize_rows_int8", "gqa_attn_prefill_plan", "gqa_abi_version",
-            "gqa_status_string"} <= set(names)
+            "gqa_attn_prefill_qint8", "gqa_quantize_rows_int8", "gqa_attn_prefill_plan",
+            "gqa_abi_version", "gqa_status_string"} <= set(names)
     lib = ctypes.CDLL(gqa_build.LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -52,7 +52,7 @@ def test_probe_library_loads():
 
 
 def test_abi_version_and_status_strings():
-    assert binding.gqa_abi_version() == 2
+    assert binding.gqa_abi_version() == 3
     for s in range(7):
         assert binding.gqa_status_string(s)
     assert binding.gqa_status_string(99) == "unknown status"
@@ -190,3 +190,37 @@ def test_plan_reports_segments():
     plan = binding.gqa_attn_prefill_plan(512, 32768, paged=True)
     assert "workgroups=256" in plan and "segments=4" in plan
     assert f"workspace_bytes={SPLIT_512x32768}" in plan
+
+
+def qint8_call(qc=16, qs=16, k=16, v=16, bt=None, nb=0, ks=16, q_len=4, kv_len=8, out=16,
+               ws=None, ws_bytes=0):
+    lib = binding.library()
+    vp = ctypes.c_void_p
+    return lib.gqa_attn_prefill_qint8(vp(qc), vp(qs), vp(k), vp(v), vp(bt), nb, vp(ks), q_len,
+                                      kv_len, vp(out), vp(ws), ws_bytes, None)
+
+
+def test_qint8_argument_errors_return_before_launch():
+    # every case below is refused on the host, so no kernel is launched
+    assert qint8_call(qc=None, qs=None, k=None, v=None, ks=None, out=None, q_len=0) == OK
+    assert qint8_call(qs=None) == NULL
+    assert qint8_call(ks=None) == NULL       # the codes are only meaningful with INT8 keys
+    assert qint8_call(qc=None) == NULL
+    assert qint8_call(qs=16 + 2) == MISALIGNED
+    assert qint8_call(qc=16 + 8) == MISALIGNED
+    assert qint8_call(ks=16 + 1) == MISALIGNED
+    assert qint8_call(q_len=9, kv_len=8) == BADLEN
+    assert qint8_call(bt=16, nb=0, kv_len=40) == BADLEN
+    # a shape that splits needs the workspace gqa_attn_prefill_ws would need
+    need = binding.gqa_attn_prefill_workspace_size(512, 32768, int8k=True)
+    assert need > 0
+    assert qint8_call(q_len=512, kv_len=32768) == WORKSPACE
+    assert qint8_call(q_len=512, kv_len=32768, ws=4096, ws_bytes=need - 1) == WORKSPACE
+
+
+def test_qint8_binding_checks_dtypes():
+    import torch
+    q = torch.zeros((4, 24, 256), dtype=torch.int8)
+    with pytest.raises(ValueError):   # k_scale is required
+        binding.gqa_attn_prefill_qint8(q, torch.zeros((4, 24)), torch.zeros((8, 4, 256),
+                                       dtype=torch.int8), torch.zeros((8, 4, 256)))

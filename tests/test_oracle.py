@@ -397,6 +397,32 @@ def test_int8_reduces_to_float_when_quantisation_is_exact():
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
 
 
+def test_int8_codes_reduce_to_float_attention_on_dequantised_values():
+    """attention_int8 on arbitrary codes and float32 scales (not the quantiser's) equals
+    float attention on Qq·sQ and Kq·sK: the products are exact in float64, so only the
+    order of the score arithmetic differs."""
+    rng = np.random.default_rng(18)
+    q_len, kv_len = 6, 23
+    qq = rng.integers(-127, 128, (q_len, HQ, D)).astype(np.int8)
+    kq = rng.integers(-127, 128, (kv_len, HKV, D)).astype(np.int8)
+    sq = (rng.random((q_len, HQ)) * 0.02 + 1e-3).astype(np.float32)
+    ks = (rng.random((kv_len, HKV)) * 0.02 + 1e-3).astype(np.float32)
+    sq[2, 7] = 0.0   # a zero row: uniform weights over its keys
+    v = rng.standard_normal((kv_len, HKV, D))
+    got = oracle.attention_int8(qq, sq, kq, ks, v)
+    q = qq.astype(np.float64) * sq[..., None].astype(np.float64)
+    k = kq.astype(np.float64) * ks[..., None].astype(np.float64)
+    np.testing.assert_allclose(got, oracle.attention(q, k, v), rtol=0, atol=1e-12)
+    off = kv_len - q_len
+    np.testing.assert_allclose(got[2, 7], v[:off + 3, 1].mean(0), atol=1e-12)
+    # the quantising form is this one on the quantiser's codes
+    qb, kb, vb, _ = make_qkv(4, 30, seed=19)
+    kq2, ks2 = oracle.quantize_rows_int8(kb)
+    qq2, sq2 = oracle.quantize_rows_int8(qb)
+    np.testing.assert_array_equal(oracle.attention_int8k(qb, kq2, ks2, vb),
+                                  oracle.attention_int8(qq2, sq2, kq2, ks2, vb))
+
+
 def test_int8_scores_within_closed_form_bound():
     """|Sq - S| <= (sQ/2) sum|k| + (sK/2) sum|q| + 256 sQ sK / 4, all over 16."""
     q, k, _, _ = make_qkv(6, 20, seed=16)
