@@ -1096,6 +1096,35 @@ __global__ __launch_bounds__(256) void merge_segments_kernel(const float* ws_o, 
   }
 }
 
+// The same merge for many output rows (a prefill chunk cut into a few segments), where a
+// workgroup per row quarter would spend more time starting than loading: one wave per
+// row, a lane four features, so each segment's part of the row is one contiguous KiB.
+// The segments are summed in order.
+__global__ __launch_bounds__(256) void merge_rows_kernel(const float* ws_o, const float* ws_ml,
+                                                         int n_seg, int64_t rows, uint8_t* out) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml);
+  float mmax = -__builtin_inff();
+  for (int sg = 0; sg < n_seg; ++sg) {
+    const float2 v = ml[sg * rows + row];
+    mmax = v.y > 0.0f ? fmaxf(mmax, v.x) : mmax;
+  }
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float lsum = 0.0f;
+  for (int sg = 0; sg < n_seg; ++sg) {
+    const float2 v = ml[sg * rows + row];
+    const f32x4 o = *reinterpret_cast<const f32x4*>(ws_o + (size_t)(sg * rows + row) * kD + 4 * lane);
+    const bool used = v.y > 0.0f;
+    const float wgt = __builtin_amdgcn_exp2f(v.x - mmax);
+    acc += used ? wgt * o : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    lsum += used ? wgt * v.y : 0.0f;
+  }
+  const bf16x4 y = __builtin_convertvector(acc * (1.0f / lsum), bf16x4);
+  *reinterpret_cast<bf16x4*>(out + ((size_t)row * kD + 4 * lane) * 2) = y;
+}
+
 // ---- standalone row quantiser: one wave per 256-element row ----
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint8_t* x, int64_t rows,
                                                             int8_t* xq, float* scale) {
@@ -1209,6 +1238,10 @@ int segments_for(int32_t q_len, int32_t kv_len, const Launch& lc) {
   return best;
 }
 
+// Output rows from which the merge runs a wave per row (merge_rows_kernel: 256 rows
+// already give every compute unit a workgroup) instead of a workgroup per row quarter.
+constexpr int64_t kMergeRowsMin = 1024;
+
 size_t workspace_bytes_for(int32_t q_len, int n_seg) {
   if (n_seg <= 1) return 0;
   return (size_t)n_seg * q_len * kHq * (kD + 2) * sizeof(float);
@@ -1301,8 +1334,12 @@ int prefill(const void* q, const float* q_scale, const void* k, const void* v,
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
   if (n_seg > 1) {
     const int64_t rows = (int64_t)q_len * kHq;
-    hipLaunchKernelGGL(merge_segments_kernel, dim3((unsigned)rows, kD / 64), dim3(256), 0, s,
-                       p.ws_o, p.ws_ml, n_seg, rows, p.out);
+    if (rows >= kMergeRowsMin)
+      hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+                         p.ws_o, p.ws_ml, n_seg, rows, p.out);
+    else
+      hipLaunchKernelGGL(merge_segments_kernel, dim3((unsigned)rows, kD / 64), dim3(256), 0, s,
+                         p.ws_o, p.ws_ml, n_seg, rows, p.out);
     if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
   }
   return GQA_OK;
