@@ -20,12 +20,16 @@
 //     of the 16x16 MFMA output: block b = one query head, column c = one token
 //     of a 16-token run. QB = 3 (the default): a workgroup is 32 tokens x all 6
 //     heads of g (192 rows); QB = 2: 64 tokens x a pair of g's heads (128 rows);
+//     QB = 1, for chunks of at most 4 tokens (decode): a wave is one token and
+//     column c is head 6 g + c ([INT8 QK §5.1]: 6 live columns of 16);
+//   * long histories with few query rows are cut into KV segments whose partial
+//     results a second kernel merges by the log-sum-exp rule ([INT8 QK §4]);
 //   * scores are computed transposed (S^T = K·Q^T) so every lane holds keys of
 //     ONE query column, and the lane's S^T registers are directly the P^T operand
 //     of the P·V MFMA;
 //   * KV tiles of 64 keys arrive by buffer loads that write LDS directly (no
-//     staging registers), double-buffered, issued a few per MFMA step over the
-//     whole iteration; rows are stored in 128-byte segments with an XOR swizzle so
+//     staging registers), double-buffered, issued one or two per MFMA step of the
+//     Q·K^T part of an iteration; rows are stored in 128-byte segments with an XOR swizzle so
 //     that K fragments are conflict-free ds_read_b128 and the V^T operand of P·V
 //     is two conflict-free ds_read_b64_tr_b16 transposing reads;
 //   * software pipeline: iteration j turns S(j) into P(j) while the MFMAs of
@@ -41,8 +45,10 @@
 //   * the output accumulator lives in the accumulation registers (AGPRs), scores,
 //     P and fragments in the architectural VGPRs;
 //   * with INT8 keys each query row is quantised in the prologue (once per row,
-//     [INT8 QK §4]) and Q·K^T runs on v_mfma_i32_16x16x64_i8; the int32 score is
-//     scaled by sK·sQ·log2(e)/16 per score before the softmax ([INT8 QK §1]).
+//     [INT8 QK §4]) unless the caller hands in its codes, and Q·K^T runs on
+//     v_mfma_i32_16x16x64_i8; the int32 score is scaled by sK·sQ·log2(e)/16 per
+//     score before the softmax ([INT8 QK §1]), for the next tile during the P·V
+//     steps of the current one.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
