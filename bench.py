@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=3,
                     help="1 tiny, 2 4096x8192, 3 4096x32768 (default), 4 paged 512x32768, "
                          "5 int8-k 3072x16384, 6 4096x16384, 7 paged int8-k 512x32768, "
-                         "8 decode 1x32768, 9 paged decode 1x32768")
+                         "8 decode 1x32768, 9 paged decode 1x32768, "
+                         "10 paged int8-k decode 1x32768")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="query rows of the workload the CPU oracle computes (all 24 heads)")

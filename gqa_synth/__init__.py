@@ -66,6 +66,8 @@ WORKLOADS = {
     7: Workload("paged_int8k_512x32768", 512, 32768, paged=True, int8k=True, num_blocks=2048, seed=7),
     8: Workload("decode_1x32768", 1, 32768, seed=8),
     9: Workload("decode_paged_1x32768", 1, 32768, paged=True, num_blocks=2048, seed=9),
+    10: Workload("decode_paged_int8k_1x32768", 1, 32768, paged=True, int8k=True, num_blocks=2048,
+                 seed=10),
 }
 
 

@@ -127,3 +127,23 @@ def test_full_size_decode():
     mx, mean = errors(out, oracle.attention(d["q"], d["k"], d["v"]))
     note(f"  max {mx:.3e} mean {mean:.3e}")
     assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+def test_full_size_paged_int8k_decode():
+    """The INT8 QK page's decode case: one token over 32768 keys of a paged split-d INT8
+    K cache, as the benchmark times it (KV segments through a workspace); every output
+    against the oracle on the oracle's codes."""
+    w = WORKLOADS[10]
+    note(f"case {w.name}: {decode_plan(w.q_len, w.kv_len, paged=True, int8k=True)}")
+    d = make_workload(w)
+    kq, ks = oracle.quantize_rows_int8(d["k"])
+    bt = d["block_table"]
+    kc = scatter_paged_int8_splitd(torch.from_numpy(kq), bt, w.num_blocks)
+    sc = scatter_paged_scales(torch.from_numpy(ks), bt, w.num_blocks)
+    out = gqa.gqa_attn_prefill_ws(d["q"].to(DEV), kc.to(DEV), d["v_cache"].to(DEV),
+                                  block_table=bt.to(DEV), k_scale=sc.to(DEV), kv_len=w.kv_len)
+    torch.cuda.synchronize()
+    ref = oracle.attention_int8k(d["q"], kq, ks, d["v"])
+    e = np.abs(out.float().cpu().numpy().astype(np.float64) - ref)
+    note(f"  max {e.max():.3e}")
+    assert e.max() <= INT8_MAX
