@@ -171,7 +171,14 @@ __device__ __forceinline__ size_t kv_row(int g, int key, int blk) {
 //                             four of each parity over its four 32-byte bank groups)
 // A global->LDS copy instruction moves 8 keys x one 128-byte segment: every lane
 // group of 8 reads one whole 128-byte line of a key row.
+//
+// Paged INT8 K (the split-d cache below) keeps the cache's own page order instead:
+// the 16 keys of a 16-key block kb form one 4 KiB page, chunk (16 features) ch of key
+// k at kb * 4096 + ch * 256 + (k & 15) * 16. A copy instruction is then 1 KiB of a
+// page, contiguous on both sides, and a fragment read (16 keys x one chunk per lane
+// group) is 1 KiB of consecutive LDS, conflict-free without a swizzle.
 constexpr int kSegStride = kKt * 128;   // 8 KiB
+constexpr int kPageBytes = kBs * kD;    // 4 KiB: 16 keys x 256 int8 features
 
 template <bool V>
 __device__ __forceinline__ int tile_swizzle(int key) {
@@ -203,37 +210,41 @@ __device__ __forceinline__ lds_void* lds_ptr(uint32_t addr) {
 
 // SPLITD: the paged INT8 K cache of "gfx936 DCU上实现INT8 QK MMAC" §3, laid out
 // [block, kv_head, 256 / 16, 16 slots, 16]: a (block, head) page is 16 chunks of 16
-// features, each holding that chunk for all 16 slots. Feature chunk c of slot k sits at
-// c * 256 + k * 16 in the page, so a 128-byte segment (8 chunks) of a key row is read
-// from 8 places 256 bytes apart and consecutive segments are 2048 bytes apart. The
-// slots of a page are interleaved, so the descriptor covers the whole 4 KiB page; slots
-// past kv_len hold whatever the cache holds (finite int8 codes) and their scales, which
-// are zeroed (ScaleCopy), make their scores 0 before the causal mask hides them.
+// features, each holding that chunk for all 16 slots (chunk c of slot k at c * 256 +
+// k * 16). The wave copies its page as it is, 1 KiB per instruction, into the
+// page-major tile above. The slots of a page are interleaved, so the descriptor covers
+// the whole 4 KiB page; slots past kv_len hold whatever the cache holds (finite int8
+// codes) and their scales, which are zeroed (ScaleCopy), make their scores 0 before the
+// causal mask hides them.
 template <bool PAGED, int ROW_BYTES, bool V, bool SPLITD = false>
 struct WaveCopy {
   static_assert(!SPLITD || (PAGED && ROW_BYTES == kD), "the split-d layout is the paged INT8 K cache");
   static constexpr int kNseg = ROW_BYTES / 128;                      // 128-byte segments per row
   static constexpr int kInsts = 2 * kNseg;                          // 8 keys x one segment each
   static constexpr int kStride = PAGED ? ROW_BYTES : kHkv * ROW_BYTES;   // bytes between keys
-  static constexpr int kSegSrc = SPLITD ? 8 * kBs * 16 : 128;      // source bytes between segments
 
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t lds;   // LDS address of the wave's first row, segment 0, in the destination tile
 
   // Source offset of lane (kr = lane / 8, physical piece pp = lane % 8) for key half `half`:
-  // the lane fetches the logical piece that the tile swizzle stores at position pp.
+  // the lane fetches the logical piece that the tile swizzle stores at position pp
+  // (SPLITD: byte 16 lane of each KiB of the page).
   static __device__ __forceinline__ uint32_t lane_offset(int lane, int half) {
-    const int kr = lane >> 3, pp = lane & 7;
-    const int piece = pp ^ tile_swizzle<V>(kr);
-    if constexpr (SPLITD)
-      return (uint32_t)(piece * kBs * 16 + (8 * half + kr) * 16);
-    else
+    if constexpr (SPLITD) {
+      (void)half;
+      return (uint32_t)(lane * 16);
+    } else {
+      const int kr = lane >> 3, pp = lane & 7;
+      const int piece = pp ^ tile_swizzle<V>(kr);
       return (uint32_t)((8 * half + kr) * kStride + (piece << 4));
+    }
   }
 
-  // first = kbase + 16 w (wave-uniform); lds_rows = destination tile + 16 w rows
+  // first = kbase + 16 w (wave-uniform); blk = the physical block holding it (paged);
+  // lds_rows = the wave's first row (segment 0) in the destination tile, or (SPLITD) its
+  // page
   __device__ __forceinline__ WaveCopy(const Params& p, const uint8_t* base, int g, int first,
-                                      uint32_t lds_rows) {
+                                      int blk, uint32_t lds_rows) {
     const int n = min(max(p.kv_len - first, 0), 16);   // rows of this wave before kv_len
     int bytes;
     if constexpr (SPLITD)
@@ -244,21 +255,26 @@ struct WaveCopy {
     const int nrec = __builtin_amdgcn_readfirstlane(bytes);
     const uint8_t* wb;
     if constexpr (PAGED) {
-      const int blk = min(max(p.bt[min(first, p.kv_len - 1) >> 4], 0), p.num_blocks - 1);
       wb = base + (size_t)(blk * kHkv + g) * kBs * ROW_BYTES;
     } else {
+      (void)blk;
       wb = base + ((size_t)first * kHkv + g) * ROW_BYTES;   // not dereferenced when n == 0
     }
     rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wb), (short)0, nrec, 0x00020000);
     lds = lds_rows;
   }
 
-  // Instruction I: key half I / kNseg, segment I % kNseg.
+  // Instruction I: key half I / kNseg, segment I % kNseg; SPLITD: KiB I of the page.
   template <int I>
   __device__ __forceinline__ void issue(const uint32_t (&voff)[2]) const {
-    constexpr int half = I / kNseg, sg = I % kNseg;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds + half * 1024 + sg * kSegStride), 16,
-                                             voff[half], sg * kSegSrc, 0, 0);
+    if constexpr (SPLITD) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds + I * 1024), 16, voff[0], I * 1024,
+                                               0, 0);
+    } else {
+      constexpr int half = I / kNseg, sg = I % kNseg;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds + half * 1024 + sg * kSegStride), 16,
+                                               voff[half], sg * 128, 0, 0);
+    }
   }
 };
 
@@ -280,15 +296,15 @@ struct ScaleCopy {
     else
       return (uint32_t)((lane & 15) * kHkv * 4 + (lane >> 4) * 4);
   }
-  __device__ __forceinline__ ScaleCopy(const Params& p, int first, uint32_t lds_block) {
+  __device__ __forceinline__ ScaleCopy(const Params& p, int first, int blk, uint32_t lds_block) {
     n = __builtin_amdgcn_readfirstlane(min(max(p.kv_len - first, 0), 16));
     const uint8_t* wb;
     int bytes;
     if constexpr (PAGED) {
-      const int blk = min(max(p.bt[min(first, p.kv_len - 1) >> 4], 0), p.num_blocks - 1);
       wb = reinterpret_cast<const uint8_t*>(p.ks) + (size_t)blk * kHkv * kBs * 4;
       bytes = n > 0 ? kHkv * kBs * 4 : 0;
     } else {
+      (void)blk;
       wb = reinterpret_cast<const uint8_t*>(p.ks) + (size_t)first * kHkv * 4;
       bytes = n * kHkv * 4;
     }
@@ -334,18 +350,26 @@ __device__ __forceinline__ void lds_wait4(u32x4& a, u32x4& b, u32x4& c, u32x4& d
 // Lane (L, c) reads K fragment (kb, s) = key 16 kb + c, piece 4 s + L:
 //   (s >> 1) * kSegStride + kb * 2048 + c * 128 + (((4 (s & 1) + L) ^ (c & 7)) << 4)
 // i.e. one of two per-lane bases (s even / odd) plus an immediate offset.
-template <bool INT8K, int QB>
+template <bool INT8K, int QB, bool PM = false>
 struct QK {
+  static_assert(!PM || INT8K, "the page-major K tile holds INT8 keys");
   using Acc = typename std::conditional<INT8K, i32x4, f32x4>::type;
   using Frag = typename std::conditional<INT8K, i32x4, bf16x8>::type;
   static constexpr int kSteps = INT8K ? 4 : 8;
 
   // Fragments kb = KB0, KB0 + 1 of K step s; `base` = the lane's even- or odd-step base.
+  // PM (page-major tile): lane (L, c) reads chunk 4 s + L of key 16 kb + c at
+  // kb * 4096 + s * 1024 + L * 256 + c * 16, one base for every step.
   template <int S, int KB0>
   static __device__ __forceinline__ void issue(u32x4 (&f)[2], uint32_t base_even, uint32_t base_odd) {
-    const uint32_t base = (S & 1) ? base_odd : base_even;
-    f[0] = lds_read_b128<(S >> 1) * kSegStride + (KB0 + 0) * 2048>(base);
-    f[1] = lds_read_b128<(S >> 1) * kSegStride + (KB0 + 1) * 2048>(base);
+    if constexpr (PM) {
+      f[0] = lds_read_b128<S * 1024 + (KB0 + 0) * kPageBytes>(base_even);
+      f[1] = lds_read_b128<S * 1024 + (KB0 + 1) * kPageBytes>(base_even);
+    } else {
+      const uint32_t base = (S & 1) ? base_odd : base_even;
+      f[0] = lds_read_b128<(S >> 1) * kSegStride + (KB0 + 0) * 2048>(base);
+      f[1] = lds_read_b128<(S >> 1) * kSegStride + (KB0 + 1) * 2048>(base);
+    }
   }
 
   static __device__ __forceinline__ Acc mfma(const u32x4& k, const Frag& q, const Acc& c) {
@@ -364,11 +388,11 @@ __device__ __forceinline__ void lds_wait2(u32x4& a, u32x4& b) {
 // One K step S over key blocks KB0, KB0 + 1 (32 keys): wait for its 2 fragments
 // (the next step's 2 reads may stay in flight), issue the reads of step S + 1, run
 // its 2 x QB MFMAs, then `extra(S)`.
-template <bool INT8K, int QB, int KB0, int S, class Extra>
+template <bool INT8K, int QB, bool PM, int KB0, int S, class Extra>
 __device__ __forceinline__ void qk_half(u32x4 (&kf)[2][2], uint32_t be, uint32_t bo,
                                         const typename QK<INT8K, QB>::Frag (&qf)[QB][QK<INT8K, QB>::kSteps],
                                         typename QK<INT8K, QB>::Acc (&acc)[QB][4], Extra&& extra) {
-  using Q = QK<INT8K, QB>;
+  using Q = QK<INT8K, QB, PM>;
   if constexpr (S + 1 < Q::kSteps) {
     Q::template issue<S + 1, KB0>(kf[(S + 1) & 1], be, bo);
     lds_wait2<2>(kf[S & 1][0], kf[S & 1][1]);
@@ -381,18 +405,18 @@ __device__ __forceinline__ void qk_half(u32x4 (&kf)[2][2], uint32_t be, uint32_t
     for (int b = 0; b < QB; ++b)
       acc[b][KB0 + kk] = Q::mfma(kf[S & 1][kk], qf[b][S], acc[b][KB0 + kk]);
   extra(std::integral_constant<int, S>{});
-  if constexpr (S + 1 < Q::kSteps) qk_half<INT8K, QB, KB0, S + 1>(kf, be, bo, qf, acc, extra);
+  if constexpr (S + 1 < Q::kSteps) qk_half<INT8K, QB, PM, KB0, S + 1>(kf, be, bo, qf, acc, extra);
 }
 
 // All K steps over key blocks KB0, KB0 + 1 of the tile at LDS address `kbuf`.
-template <bool INT8K, int QB, int KB0, class Extra>
+template <bool INT8K, int QB, bool PM, int KB0, class Extra>
 __device__ __forceinline__ void qk_pair(uint32_t kbuf, int kb_even, int kb_odd,
                                         const typename QK<INT8K, QB>::Frag (&qf)[QB][QK<INT8K, QB>::kSteps],
                                         typename QK<INT8K, QB>::Acc (&acc)[QB][4], Extra&& extra) {
-  using Q = QK<INT8K, QB>;
+  using Q = QK<INT8K, QB, PM>;
   u32x4 kf[2][2];
   Q::template issue<0, KB0>(kf[0], kbuf + kb_even, kbuf + kb_odd);
-  qk_half<INT8K, QB, KB0, 0>(kf, kbuf + kb_even, kbuf + kb_odd, qf, acc, extra);
+  qk_half<INT8K, QB, PM, KB0, 0>(kf, kbuf + kb_even, kbuf + kb_odd, qf, acc, extra);
 }
 
 // ---- O^T += V^T · P^T (and l += 1 · P^T) ----
@@ -525,7 +549,8 @@ constexpr int lds_bytes() {
 template <bool PAGED, bool INT8K, int QB, bool SPLIT>
 __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   using S = Shape<QB>;
-  using Q = QK<INT8K, QB>;
+  constexpr bool kPM = PAGED && INT8K;   // page-major K tiles (the split-d cache)
+  using Q = QK<INT8K, QB, kPM>;
   using Acc = typename Q::Acc;
   constexpr int kKTile = k_tile_bytes<PAGED, INT8K, QB>();
   constexpr int kVOff = 2 * kKTile;                    // V tiles follow the two K tiles
@@ -588,23 +613,40 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   const uint32_t vvo[2] = {VCopy::lane_offset(lane, 0), VCopy::lane_offset(lane, 1)};
   const uint32_t svo = SCopy::lane_offset(lane);
   const int skey = lane & 15;   // the key whose scales this lane copies
-  auto kcopy = [&](int kbase, int buf) {
-    return KCopy(p, p.k, g, kbase + 16 * w, smem_addr + buf * kKTile + 16 * w * 128);
+  // Paged: the physical block of this wave's 16 keys of the tile at kbase (an entry
+  // outside [0, num_blocks) is clamped into it); 0 when contiguous. The block table is
+  // read-only for the whole launch, so it is read as constant memory: a scalar load
+  // into a scalar register, which a loop-carried value can wait in until its use.
+  auto block_of = [&](int kbase) -> int {
+    if constexpr (PAGED) {
+      const int first = __builtin_amdgcn_readfirstlane(min(kbase + 16 * w, p.kv_len - 1));
+      const int entry = *(const __attribute__((address_space(4))) int32_t*)(p.bt + (first >> 4));
+      return min(max(entry, 0), p.num_blocks - 1);
+    } else {
+      (void)kbase;
+      return 0;
+    }
   };
-  auto vcopy = [&](int kbase, int buf) {
-    return VCopy(p, p.v, g, kbase + 16 * w, smem_addr + kVOff + buf * 4 * kSegStride + 16 * w * 128);
+  auto kcopy = [&](int kbase, int buf, int blk) {
+    return KCopy(p, p.k, g, kbase + 16 * w, blk,
+                 smem_addr + buf * kKTile + (kPM ? w * kPageBytes : 16 * w * 128));
   };
-  auto scopy = [&](int kbase, int slot) {
-    return SCopy(p, kbase + 16 * w, sk_addr + slot * kSkTile + w * 256);
+  auto vcopy = [&](int kbase, int buf, int blk) {
+    return VCopy(p, p.v, g, kbase + 16 * w, blk,
+                 smem_addr + kVOff + buf * 4 * kSegStride + 16 * w * 128);
+  };
+  auto scopy = [&](int kbase, int slot, int blk) {
+    return SCopy(p, kbase + 16 * w, blk, sk_addr + slot * kSkTile + w * 256);
   };
   // whole-tile copies outside the pipelined loop
   auto copy_k_all = [&](int kbase, int buf, int slot) {
-    const KCopy kc = kcopy(kbase, buf);
+    const int blk = block_of(kbase);
+    const KCopy kc = kcopy(kbase, buf, blk);
     static_for<0, KCopy::kInsts>([&](auto ic) { kc.template issue<decltype(ic)::value>(kvo); });
-    if constexpr (INT8K) scopy(kbase, slot).issue(svo, skey);
+    if constexpr (INT8K) scopy(kbase, slot, blk).issue(svo, skey);
   };
   auto copy_v_all = [&](int kbase, int buf) {
-    const VCopy vc = vcopy(kbase, buf);
+    const VCopy vc = vcopy(kbase, buf, block_of(kbase));
     static_for<0, VCopy::kInsts>([&](auto ic) { vc.template issue<decltype(ic)::value>(vvo); });
   };
 
@@ -682,8 +724,8 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   }
 
   // ---- per-lane LDS bases ----
-  const int kb_even = c * 128 + ((L ^ (c & 7)) << 4);
-  const int kb_odd = c * 128 + (((L ^ (c & 7)) ^ 4) << 4);
+  const int kb_even = kPM ? L * 256 + c * 16 : c * 128 + ((L ^ (c & 7)) << 4);
+  const int kb_odd = kPM ? kb_even : c * 128 + (((L ^ (c & 7)) ^ 4) << 4);
   uint32_t vbase_off[4];
   const int vsw = tile_swizzle<true>(4 * L + (c >> 2)) >> 1;   // V swizzle of this lane's key
 #pragma unroll
@@ -707,8 +749,8 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     for (int b = 0; b < QB; ++b)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) sacc[b][kb] = Acc{0, 0, 0, 0};
-    qk_pair<INT8K, QB, 0>(kbuf, kb_even, kb_odd, qf, sacc, [](auto) {});
-    qk_pair<INT8K, QB, 2>(kbuf, kb_even, kb_odd, qf, sacc, [](auto) {});
+    qk_pair<INT8K, QB, kPM, 0>(kbuf, kb_even, kb_odd, qf, sacc, [](auto) {});
+    qk_pair<INT8K, QB, kPM, 2>(kbuf, kb_even, kb_odd, qf, sacc, [](auto) {});
   };
   // INT8 keys: sacc holds int32 dot products until scale_unit turns them, in place, into
   // float scores in log2 units (their bit patterns): y = float(S) * (sK * sQ * log2(e)/16),
@@ -861,6 +903,14 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     // buffer nothing reads again, and the restart flag is rewritten every tile.
     const int n_plain = min(j1, (off + t0 + 1) / kKt);
     int flag_seen = 0;   // flags read after the previous tile's barrier
+    // first key of the tile that iteration j copies (K and scales of tile j + 2, V of tile
+    // j + 1); a tile past the segment is fetched from kv_len on: no rows, no traffic
+    auto copy_base = [&](int tile) { return tile < j1 ? tile * kKt : p.kv_len; };
+    // Paged: block-table entries are read one iteration before their copies (the value
+    // for iteration j + 1's K copy is loaded at the start of iteration j), so a copy never
+    // waits for its block-table read.
+    int blk_v = block_of(copy_base(j0 + 1));   // V copy of the current iteration
+    int blk_k = block_of(copy_base(j0 + 2));   // K and scale copies of the current iteration
     // returns true when pass 0 must restart
     auto body = [&](int j, auto mask_c) -> bool {
       const int kbase = j * kKt;
@@ -871,13 +921,15 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       // so the 64 KiB of a tile need a good part of the iteration, and issuing them in a
       // burst would stall the waves on a full address queue; the P·V steps, three MFMAs
       // each, leave too little time between copies (measured)
-      // (a tile past the segment is fetched from kv_len on: no rows, no traffic)
-      const int kb2 = j + 2 < j1 ? kbase + 2 * kKt : p.kv_len;
-      const int kb1 = j + 1 < j1 ? kbase + kKt : p.kv_len;
-      const KCopy kc = kcopy(kb2, j & 1);
-      const VCopy vc = vcopy(kb1, (j + 1) & 1);
+      const int kb2 = copy_base(j + 2);
+      const int kb1 = copy_base(j + 1);
+      const int blk_next = block_of(copy_base(j + 3));
+      const KCopy kc = kcopy(kb2, j & 1, blk_k);
+      const VCopy vc = vcopy(kb1, (j + 1) & 1, blk_v);
       SCopy scp;
-      if constexpr (INT8K) scp = scopy(kb2, (j + 2) % 3);
+      if constexpr (INT8K) scp = scopy(kb2, (j + 2) % 3, blk_k);
+      blk_v = blk_k;
+      blk_k = blk_next;
       constexpr int kCopies = KCopy::kInsts + VCopy::kInsts + (INT8K ? 1 : 0);
       auto copy_issue = [&](auto ic) {
         constexpr int I = decltype(ic)::value;
@@ -927,7 +979,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
             }
           }
         };
-        qk_pair<INT8K, QB, 2 * H>(kn, kb_even, kb_odd, qf, sacc, softmax_part);
+        qk_pair<INT8K, QB, kPM, 2 * H>(kn, kb_even, kb_odd, qf, sacc, softmax_part);
       };
       half(std::integral_constant<int, 0>{});
       half(std::integral_constant<int, 1>{});

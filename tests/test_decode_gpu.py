@@ -117,12 +117,18 @@ def test_decode_restart():
         assert mx <= BF16_MAX and mean <= BF16_MEAN
 
 
-def test_full_size_decode():
-    """The decode workload the benchmark times (1 token over 32768 keys), every output."""
-    w = WORKLOADS[8]
-    note(f"case {w.name}: {decode_plan(w.q_len, w.kv_len)}")
+@pytest.mark.parametrize("idx", [8, 9])
+def test_full_size_decode(idx):
+    """The decode workloads the benchmark times (1 token over 32768 keys, contiguous and
+    paged), every output."""
+    w = WORKLOADS[idx]
+    note(f"case {w.name}: {decode_plan(w.q_len, w.kv_len, paged=w.paged)}")
     d = make_workload(w)
-    out = gqa.gqa_attn_prefill_ws(d["q"].to(DEV), d["k"].to(DEV), d["v"].to(DEV))
+    if w.paged:
+        out = gqa.gqa_attn_prefill_ws(d["q"].to(DEV), d["k_cache"].to(DEV), d["v_cache"].to(DEV),
+                                      block_table=d["block_table"].to(DEV), kv_len=w.kv_len)
+    else:
+        out = gqa.gqa_attn_prefill_ws(d["q"].to(DEV), d["k"].to(DEV), d["v"].to(DEV))
     torch.cuda.synchronize()
     mx, mean = errors(out, oracle.attention(d["q"], d["k"], d["v"]))
     note(f"  max {mx:.3e} mean {mean:.3e}")
