@@ -90,8 +90,14 @@ def cpu_baseline(w, d, rows_n):
     else:
         oracle.attention(d["q"], d["k"], d["v"], rows=rows)
     dt = time.perf_counter() - t
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:  # pragma: no cover
+        pass
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(dt, 3),
+            "cpu": cpu, "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"query rows {rows[0]}..{rows[-1]} ({rows_n} rows) x 24 heads of {w.name}"}
 
 
