@@ -106,10 +106,12 @@ struct Params {
   int32_t q_len;
   int32_t kv_len;
   int32_t n_tblk;          // token blocks of the grid
-  int32_t n_seg;           // KV segments per (KV head, token block); 1 = the whole history
-  float* ws_o;             // n_seg > 1: unnormalised O [n_seg, q_len, 24, 256]
-  float* ws_ml;            // n_seg > 1: (reference maximum, row sum) [n_seg, q_len, 24, 2]
+  int32_t n_seg;           // KV segments per split (KV head, token block); 1 = none split
+  int32_t n_plain;         // n_seg > 1: the shortest token blocks 0 .. n_plain - 1 run whole
+  float* ws_o;             // n_seg > 1: unnormalised O [n_seg, split rows, 24, 256]
+  float* ws_ml;            // n_seg > 1: (reference maximum, row sum) [n_seg, split rows, 24, 2]
 };
+
 
 // Workgroup shape for QB 16-column query blocks per wave. QB = 3 and QB = 2 map a
 // column to a token (16-token runs) and a block to a query head. QB = 1 is the decode
@@ -126,6 +128,37 @@ struct Shape {
   static constexpr int kTokPerWg = kDecode ? kWaves : 16 * kTokenBlocks;    // 4, 32 or 64
   static constexpr int kSplitsPerGroup = kGroup / kHeadsPerWg;      // 1 or 3 workgroups per (g, tokens)
 };
+
+// What one workgroup computes. The grid is 4 x (work units): id % 4 is the KV head, and
+// the units run in this order: first the token blocks n_plain - 1 .. 0 whole (longest
+// first), then the longer token blocks n_tblk - 1 .. n_plain, each cut into n_seg KV
+// segments (segment fastest). Only the split token blocks' rows (tokens from
+// n_plain * tokens-per-workgroup on) pass through the workspace and the merge.
+struct Unit {
+  int g, seg, nseg, hsel, tblk;
+};
+template <int QB>
+__device__ __forceinline__ Unit unit_of(const Params& p, int id) {
+  using S = Shape<QB>;
+  Unit u;
+  u.g = id & (kHkv - 1);
+  const int k = id >> 2;
+  const int plain = p.n_plain * S::kSplitsPerGroup;
+  int rest;
+  if (k < plain) {
+    u.seg = 0;
+    u.nseg = 1;
+    rest = k;
+    u.tblk = p.n_plain - 1 - rest / S::kSplitsPerGroup;
+  } else {
+    u.seg = (k - plain) % p.n_seg;
+    u.nseg = p.n_seg;
+    rest = (k - plain) / p.n_seg;
+    u.tblk = p.n_tblk - 1 - rest / S::kSplitsPerGroup;
+  }
+  u.hsel = rest % S::kSplitsPerGroup;
+  return u;
+}
 
 __device__ __forceinline__ float wave_xor_max(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask));
@@ -568,13 +601,14 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   // Workgroup id -> (KV head, KV segment, head subset, token block). id % 4 is the KV
   // head, so workgroups dispatched round-robin over the 8 XCDs keep one KV head per
   // XCD (its K/V stream shares that XCD's L2); token blocks go longest first.
-  const int id = blockIdx.x;
-  const int g = id & (kHkv - 1);
-  const int seg = (id >> 2) % p.n_seg;
-  const int rest = (id >> 2) / p.n_seg;
-  const int hsel = rest % S::kSplitsPerGroup;
-  const int tblk = p.n_tblk - 1 - rest / S::kSplitsPerGroup;
-  const int t0 = tblk * S::kTokPerWg;
+  const Unit unit = unit_of<QB>(p, blockIdx.x);
+  const int g = unit.g;
+  const int seg = unit.seg;
+  const int hsel = unit.hsel;
+  const int t0 = unit.tblk * S::kTokPerWg;
+  // workspace rows of a split token block: [segment][token - q0][head]
+  const int q0 = p.n_plain * S::kTokPerWg;
+  const size_t ws_rows = (size_t)(p.q_len - q0);
   const int off = p.kv_len - p.q_len;
   const int head0 = S::kDecode ? kGroup * g + min(c, kGroup - 1)
                                 : kGroup * g + hsel * S::kHeadsPerWg + hw * QB;   // head of block 0
@@ -591,13 +625,13 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   // 8 tiles long, so each segment starts at or before the workgroup's first query and
   // its first key is visible to every query of the workgroup (the pass-0 reference
   // below is then a real score of every column).
-  const int j0 = (int)(((int64_t)ntiles * seg) / p.n_seg);
-  const int j1 = (int)(((int64_t)ntiles * (seg + 1)) / p.n_seg);
+  const int j0 = (int)(((int64_t)ntiles * seg) / unit.nseg);
+  const int j1 = (int)(((int64_t)ntiles * (seg + 1)) / unit.nseg);
   if (j0 >= j1) {   // empty segment (not produced by the host's plans): weight 0 in the merge
     if (tok_ok && L == 0) {
 #pragma unroll
       for (int b = 0; b < QB; ++b)
-        *reinterpret_cast<float2*>(p.ws_ml + (((size_t)seg * p.q_len + tok) * kHq + head0 + b) * 2) =
+        *reinterpret_cast<float2*>(p.ws_ml + ((seg * ws_rows + (tok - q0)) * kHq + head0 + b) * 2) =
             make_float2(-__builtin_inff(), 0.0f);
     }
     return;
@@ -769,7 +803,13 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   auto scale_unit = [&](auto kb_c, auto b_c, const u32x4 (&sr)[4], auto minus_m_c) {
 #pragma clang fp contract(off)
     constexpr int kb = decltype(kb_c)::value, b = decltype(b_c)::value;
-    const f32x4 skv = __builtin_bit_cast(f32x4, sr[kb]);
+    f32x4 skv = __builtin_bit_cast(f32x4, sr[kb]);
+    // Empty volatile statements on the operand and on the result hold this unit's
+    // conversion and scaling at the P·V step that calls it: volatile statements keep
+    // their order among themselves and the P·V MFMAs are volatile statements too.
+    // Without them the compiler sinks all of a tile's scaling past the tile barrier
+    // (the restart exit does not need it), where it runs with no MFMA to overlap.
+    if constexpr (decltype(minus_m_c)::value) asm volatile("" : "+v"(sacc[b][kb]), "+v"(skv));
     f32x4 y;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -778,6 +818,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       else
         y[r] = (float)sacc[b][kb][r] * (skv[r] * qs[b]);
     }
+    if constexpr (decltype(minus_m_c)::value) asm volatile("" : "+v"(y));
     sacc[b][kb] = __builtin_bit_cast(Acc, y);
   };
   // the whole tile at once (outside the pipelined loop)
@@ -1063,11 +1104,11 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   }
 
   agpr_fence<24>(o);
-  if (p.n_seg > 1) {
+  if (unit.nseg > 1) {
     // ---- epilogue of one KV segment: unnormalised O, the reference maximum (log2
     // units, scale included) and the row sum, merged by merge_segments_kernel ----
     if (tok_ok) {
-      const size_t row0 = ((size_t)seg * p.q_len + tok) * kHq + head0;
+      const size_t row0 = (seg * ws_rows + (tok - q0)) * kHq + head0;
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
         float* orow = p.ws_o + (row0 + b) * kD;
@@ -1098,8 +1139,7 @@ template <bool PAGED, bool INT8K, int QB>
 __global__ __launch_bounds__(kThreads, 1) void gqa_prefill_kernel(const Params p) {
   using S = Shape<QB>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[lds_bytes<PAGED, INT8K, QB>()];
-  const int rest = (blockIdx.x >> 2) / p.n_seg;
-  const int t0 = (p.n_tblk - 1 - rest / S::kSplitsPerGroup) * S::kTokPerWg;
+  const int t0 = unit_of<QB>(p, blockIdx.x).tblk * S::kTokPerWg;
   if (p.kv_len - p.q_len + t0 + 1 < kSplitBelow)
     run<PAGED, INT8K, QB, true>(p, smem);
   else
@@ -1226,6 +1266,7 @@ struct Launch {
   int qb;
   int tok_per_wg;
   int n_tblk;
+  int per_tblk;      // workgroups per (KV head, token block): 1, or 3 with 2 heads each
   int workgroups;
   int threads;
   int lds_bytes;
@@ -1241,6 +1282,7 @@ Launch shape_launch(int32_t q_len, bool int8k) {
   lc.qb = QB;
   lc.tok_per_wg = S::kTokPerWg;
   lc.n_tblk = n_tblk;
+  lc.per_tblk = S::kSplitsPerGroup;
   lc.workgroups = n_tblk * kHkv * S::kSplitsPerGroup;
   lc.threads = kThreads;
   lc.lds_bytes = int8k ? lds_bytes<false, true, QB>() : lds_bytes<false, false, QB>();
@@ -1271,14 +1313,11 @@ double plan_cost(int32_t q_len, int32_t kv_len, int tok, int n_tblk, int n_seg) 
   return t;
 }
 
-// KV segments per (KV head, token block) for a call that has a workspace. A grid with a
-// workgroup for every compute unit is not split (its longest-first order balances it,
-// and splitting it further was measured to gain nothing). A smaller grid takes the
-// count with the lowest plan_cost among those that keep every segment at least
-// kMinSegTiles long in the shortest (first) token block.
-int segments_for(int32_t q_len, int32_t kv_len, const Launch& lc) {
-  const int unsplit_workgroups = lc.workgroups;
-  if (q_len == 0 || unsplit_workgroups >= kCUs) return 1;
+// KV segments per (KV head, token block) for a small grid: when the grid has fewer
+// workgroups than the 256 CUs, every token block is cut the same way, into the count
+// with the lowest plan_cost among those that keep every segment at least kMinSegTiles
+// long in the shortest (first) token block.
+int uniform_segments(int32_t q_len, int32_t kv_len, const Launch& lc) {
   const int tok = lc.tok_per_wg;
   const int n_tblk = lc.n_tblk;
   const int64_t t_min = ((int64_t)kv_len - q_len + std::min(q_len, tok) + kKt - 1) / kKt;
@@ -1296,13 +1335,117 @@ int segments_for(int32_t q_len, int32_t kv_len, const Launch& lc) {
   return best;
 }
 
+// How a call with a workspace is cut: every token block at or past n_plain into n_seg
+// KV segments (n_seg = 1: nothing is cut).
+struct SegPlan {
+  int n_seg = 1;
+  int n_plain = 0;
+};
+
+int64_t tblk_tiles(int32_t q_len, int32_t kv_len, int tok, int64_t t) {
+  const int64_t last = std::min<int64_t>((t + 1) * tok, q_len);
+  return ((int64_t)kv_len - q_len + last + kKt - 1) / kKt;
+}
+
+// Estimated run time of a plan for a grid of at least one workgroup per CU, in tile
+// times. Workgroups go round-robin to the 8 XCDs (workgroup id mod 8), so the two XCDs
+// that serve a KV head (id mod 4) take its work units alternately, and inside an XCD
+// each unit starts on the first of the 32 CUs to become free, in grid order. Each
+// workgroup adds about two tile times of prologue and epilogue, and the split rows pass
+// through the workspace and the merge (as in plan_cost).
+double plan_makespan(int32_t q_len, int32_t kv_len, const Launch& lc, const SegPlan& sp) {
+  constexpr int kCUsPerXcd = 32;
+  constexpr double kWgTiles = 2.0;
+  double free_at[2][kCUsPerXcd] = {};
+  double span = 0.0;
+  int64_t k = 0;
+  auto place = [&](double len) {
+    double* cu = free_at[k & 1];
+    int first = 0;
+    for (int i = 1; i < kCUsPerXcd; ++i)
+      if (cu[i] < cu[first]) first = i;
+    cu[first] += len + kWgTiles;
+    span = std::max(span, cu[first]);
+    ++k;
+  };
+  const int tok = lc.tok_per_wg;
+  const int64_t whole = sp.n_seg > 1 ? sp.n_plain : lc.n_tblk;   // token blocks run whole
+  for (int64_t t = whole - 1; t >= 0; --t)
+    for (int h = 0; h < lc.per_tblk; ++h) place((double)tblk_tiles(q_len, kv_len, tok, t));
+  if (sp.n_seg > 1) {
+    for (int64_t t = lc.n_tblk - 1; t >= sp.n_plain; --t) {
+      const int64_t T = tblk_tiles(q_len, kv_len, tok, t);
+      for (int h = 0; h < lc.per_tblk; ++h)
+        for (int sg = 0; sg < sp.n_seg; ++sg)
+          place((double)(T * (sg + 1) / sp.n_seg - T * sg / sp.n_seg));
+    }
+    const int64_t split_rows = (int64_t)q_len - (int64_t)sp.n_plain * tok;
+    span += 2.0 * sp.n_seg * (double)split_rows * kHq * (kD + 2) * 4 / (5e12 * 2.4e-6);
+  }
+  return span;
+}
+
+// The cut for a call that has a workspace. A grid with fewer workgroups than CUs is cut
+// uniformly (uniform_segments). A larger grid whose last round of workgroups would
+// leave CUs idle (384 workgroups on 256 CUs run in 1.5 rounds) has its longest token
+// blocks cut into 2 to 4 segments, as many as make the work units a whole number of
+// rounds (64 per KV head), when plan_makespan says that is clearly faster. Every
+// segment is at least kMinSegTiles long and every segment of a split token block starts
+// at or before the block's first query (its first key is visible to every query).
+SegPlan segments_for(int32_t q_len, int32_t kv_len, const Launch& lc) {
+  SegPlan best;
+  if (q_len == 0) return best;
+  if (lc.workgroups < kCUs) {
+    best.n_seg = uniform_segments(q_len, kv_len, lc);
+    return best;
+  }
+  constexpr int kUnitsPerRound = kCUs / kHkv;   // work units of one KV head per round
+  const int64_t units = (int64_t)lc.n_tblk * lc.per_tblk;
+  if (units % kUnitsPerRound == 0 || lc.n_tblk > 512) return best;
+  double best_cost = plan_makespan(q_len, kv_len, lc, best);
+  const int64_t k0 = (units + kUnitsPerRound - 1) / kUnitsPerRound;
+  for (int S = 2; S <= 4; ++S) {
+    for (int64_t k = k0; k <= k0 + 2; ++k) {
+      // units - n_split * per_tblk + n_split * per_tblk * S = k rounds
+      const int64_t extra = k * kUnitsPerRound - units;
+      const int64_t step = (int64_t)(S - 1) * lc.per_tblk;
+      if (extra % step != 0) continue;
+      const int64_t n_split = extra / step;
+      if (n_split < 1 || n_split >= lc.n_tblk) continue;
+      SegPlan sp;
+      sp.n_seg = S;
+      sp.n_plain = (int)(lc.n_tblk - n_split);
+      // the shortest split token block: segments long enough, and starting in the history
+      const int64_t T = tblk_tiles(q_len, kv_len, lc.tok_per_wg, sp.n_plain);
+      const int64_t first_query = (int64_t)kv_len - q_len + (int64_t)sp.n_plain * lc.tok_per_wg;
+      if (T / S < kMinSegTiles || (T * (S - 1) / S) * kKt > first_query) continue;
+      const double c = plan_makespan(q_len, kv_len, lc, sp);
+      if (c < 0.97 * best_cost) {
+        best = sp;
+        best_cost = c;
+      }
+    }
+  }
+  return best;
+}
+
 // Output rows from which the merge runs a wave per row (merge_rows_kernel: 256 rows
 // already give every compute unit a workgroup) instead of a workgroup per row quarter.
 constexpr int64_t kMergeRowsMin = 1024;
 
-size_t workspace_bytes_for(int32_t q_len, int n_seg) {
-  if (n_seg <= 1) return 0;
-  return (size_t)n_seg * q_len * kHq * (kD + 2) * sizeof(float);
+// Tokens of a call whose rows pass through the workspace (those of the split token blocks).
+int64_t split_tokens(int32_t q_len, const Launch& lc, const SegPlan& sp) {
+  return sp.n_seg > 1 ? (int64_t)q_len - (int64_t)sp.n_plain * lc.tok_per_wg : 0;
+}
+
+size_t workspace_bytes_for(int32_t q_len, const Launch& lc, const SegPlan& sp) {
+  if (sp.n_seg <= 1) return 0;
+  return (size_t)sp.n_seg * split_tokens(q_len, lc, sp) * kHq * (kD + 2) * sizeof(float);
+}
+
+int64_t grid_workgroups(const Launch& lc, const SegPlan& sp) {
+  return (int64_t)kHkv * lc.per_tblk *
+         (sp.n_plain + (int64_t)(lc.n_tblk - sp.n_plain) * sp.n_seg);
 }
 
 // Chunks of at most this many query tokens run the decode shape (4 tokens x 6 heads
@@ -1349,8 +1492,9 @@ int prefill(const void* q, const float* q_scale, const void* k, const void* v,
     if (num_blocks < need || num_blocks <= 0) return GQA_ERR_BAD_LENGTH;
   }
   const Launch lc = plan_for(q_len, kv_len, paged, int8k);
-  const int n_seg = allow_split ? segments_for(q_len, kv_len, lc) : 1;
-  const size_t ws_need = workspace_bytes_for(q_len, n_seg);
+  const SegPlan sp = allow_split ? segments_for(q_len, kv_len, lc) : SegPlan{};
+  const int n_seg = sp.n_seg;
+  const size_t ws_need = workspace_bytes_for(q_len, lc, sp);
   if (n_seg > 1) {
     if (workspace == nullptr || workspace_bytes < ws_need) return GQA_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return GQA_ERR_MISALIGNED;
@@ -1369,11 +1513,13 @@ int prefill(const void* q, const float* q_scale, const void* k, const void* v,
   p.kv_len = kv_len;
   p.n_tblk = lc.n_tblk;
   p.n_seg = n_seg;
+  p.n_plain = sp.n_plain;
+  const int64_t split_tok = split_tokens(q_len, lc, sp);
   p.ws_o = n_seg > 1 ? static_cast<float*>(workspace) : nullptr;
-  p.ws_ml = n_seg > 1 ? p.ws_o + (size_t)n_seg * q_len * kHq * kD : nullptr;
+  p.ws_ml = n_seg > 1 ? p.ws_o + (size_t)n_seg * split_tok * kHq * kD : nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(lc.workgroups * n_seg), block(lc.threads);
+  const dim3 grid((unsigned)grid_workgroups(lc, sp)), block(lc.threads);
   auto launch = [&](auto qb_c) {
     constexpr int QB = decltype(qb_c)::value;
     if (int8k && paged)
@@ -1391,13 +1537,15 @@ int prefill(const void* q, const float* q_scale, const void* k, const void* v,
     launch(std::integral_constant<int, kDefaultQB>{});
   if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
   if (n_seg > 1) {
-    const int64_t rows = (int64_t)q_len * kHq;
+    // the split token blocks' rows: the last split_tok tokens of the chunk
+    const int64_t rows = split_tok * kHq;
+    uint8_t* out_split = p.out + (size_t)(q_len - split_tok) * kHq * kD * 2;
     if (rows >= kMergeRowsMin)
       hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
-                         p.ws_o, p.ws_ml, n_seg, rows, p.out);
+                         p.ws_o, p.ws_ml, n_seg, rows, out_split);
     else
       hipLaunchKernelGGL(merge_segments_kernel, dim3((unsigned)rows, kD / 64), dim3(256), 0, s,
-                         p.ws_o, p.ws_ml, n_seg, rows, p.out);
+                         p.ws_o, p.ws_ml, n_seg, rows, out_split);
     if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
   }
   return GQA_OK;
@@ -1430,17 +1578,19 @@ int gqa_attn_prefill_plan(int32_t q_len, int32_t kv_len, int paged, int int8k, c
     return st;
   }
   const Launch lc = plan_for(q_len, kv_len, paged != 0, int8k != 0);
-  const int n_seg = segments_for(q_len, kv_len, lc);
-  snprintf(buf, n, "variant=%s workgroups=%d threads=%d lds_bytes=%d segments=%d workspace_bytes=%zu",
-           lc.name, lc.workgroups * n_seg, lc.threads, lc.lds_bytes, n_seg,
-           workspace_bytes_for(q_len, n_seg));
+  const SegPlan sp = segments_for(q_len, kv_len, lc);
+  snprintf(buf, n,
+           "variant=%s workgroups=%lld threads=%d lds_bytes=%d segments=%d whole_token_blocks=%d "
+           "workspace_bytes=%zu",
+           lc.name, (long long)grid_workgroups(lc, sp), lc.threads, lc.lds_bytes, sp.n_seg,
+           sp.n_seg > 1 ? sp.n_plain : lc.n_tblk, workspace_bytes_for(q_len, lc, sp));
   return GQA_OK;
 }
 
 size_t gqa_attn_prefill_workspace_size(int32_t q_len, int32_t kv_len, int paged, int int8k) {
   if (check_prefill_lengths(q_len, kv_len) != GQA_OK) return 0;
   const Launch lc = plan_for(q_len, kv_len, paged != 0, int8k != 0);
-  return workspace_bytes_for(q_len, segments_for(q_len, kv_len, lc));
+  return workspace_bytes_for(q_len, lc, segments_for(q_len, kv_len, lc));
 }
 
 int gqa_attn_prefill(const void* q, const void* k, const void* v, const int32_t* block_table,

@@ -159,8 +159,9 @@ def test_workspace_size():
     assert binding.gqa_attn_prefill_workspace_size(512, 32768) == SPLIT_512x32768
     assert binding.gqa_attn_prefill_workspace_size(512, 32768, paged=True) == SPLIT_512x32768
     assert binding.gqa_attn_prefill_workspace_size(512, 32768, int8k=True) == SPLIT_512x32768
-    # a grid with a workgroup for every CU is not split (3072 queries: 384 workgroups)
-    assert binding.gqa_attn_prefill_workspace_size(3072, 16384, int8k=True) == 0
+    # a grid that ends in a part-filled round (3072 queries: 384 workgroups) cuts only its
+    # longest token blocks: the rows of 1024 tokens, in 2 segments
+    assert binding.gqa_attn_prefill_workspace_size(3072, 16384, int8k=True) == 2 * 1024 * 24 * 258 * 4
     # short histories are not split below 8 tiles a segment
     assert binding.gqa_attn_prefill_workspace_size(32, 500) == 0
     # arguments the call would refuse
@@ -186,10 +187,22 @@ def test_workspace_errors_return_before_launch():
 
 def test_plan_reports_segments():
     plan = binding.gqa_attn_prefill_plan(4096, 32768)
-    assert "segments=1 workspace_bytes=0" in plan
+    assert "segments=1 whole_token_blocks=128 workspace_bytes=0" in plan
     plan = binding.gqa_attn_prefill_plan(512, 32768, paged=True)
-    assert "workgroups=256" in plan and "segments=4" in plan
+    assert "workgroups=256" in plan and "segments=4 whole_token_blocks=0" in plan
     assert f"workspace_bytes={SPLIT_512x32768}" in plan
+
+
+def test_plan_partial_split():
+    """384 workgroups (1.5 rounds on 256 CUs): the 32 longest of the 96 token blocks of
+    each KV head are cut in two, making 512 work units, two full rounds; the workspace
+    holds only those blocks' rows (1024 tokens x 24 heads x (256 + 2) floats x 2)."""
+    plan = binding.gqa_attn_prefill_plan(3072, 16384, int8k=True)
+    assert "workgroups=512" in plan and "segments=2 whole_token_blocks=64" in plan
+    assert f"workspace_bytes={2 * 1024 * 24 * 258 * 4}" in plan
+    assert binding.gqa_attn_prefill_workspace_size(3072, 16384, int8k=True) == 2 * 1024 * 24 * 258 * 4
+    # a grid of whole rounds is not cut
+    assert "segments=1" in binding.gqa_attn_prefill_plan(4096, 8192)
 
 
 def qint8_call(qc=16, qs=16, k=16, v=16, bt=None, nb=0, ks=16, q_len=4, kv_len=8, out=16,

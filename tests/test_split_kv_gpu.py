@@ -144,3 +144,70 @@ def test_split_int8k_full(q_len, kv_len):
     e = np.abs(out.float().cpu().numpy().astype(np.float64) - ref)
     note(f"  max {e.max():.3e}")
     assert e.max() <= 2e-3
+
+
+# ------------------------------------------------------------------ partial splits
+
+def plan_fields(q_len, kv_len, paged=False, int8k=False):
+    plan = gqa.gqa_attn_prefill_plan(q_len, kv_len, paged=paged, int8k=int8k)
+    return {kv.split("=")[0]: kv.split("=")[1] for kv in plan.split()}
+
+
+def region_rows(q_len, q0, n_random=12, seed=0):
+    """Rows at both ends of the whole token blocks [0, q0) and of the split ones
+    [q0, q_len), plus random rows."""
+    rng = np.random.default_rng(seed)
+    fixed = {0, 1, q0 - 33, q0 - 1, q0, q0 + 1, q0 + 31, q0 + 32, q_len - 33, q_len - 2, q_len - 1}
+    rows = sorted({r for r in fixed if 0 <= r < q_len} | set(rng.integers(0, q_len, n_random)))
+    return np.array(rows)
+
+
+# (q_len, kv_len, segments, whole token blocks of 32 tokens): grids of more than 256
+# workgroups that would end in a part-filled round have only their longest token
+# blocks cut into KV segments; the last shape has a ragged last token block
+PARTIAL_SHAPES = [(3072, 8192, 2, 64), (2112, 6000, 3, 35), (5000, 20000, 2, 122)]
+
+
+@pytest.mark.parametrize("q_len,kv_len,nseg,whole", PARTIAL_SHAPES)
+def test_partial_split_contiguous(q_len, kv_len, nseg, whole):
+    """Rows of the whole token blocks come from the same workgroup program as the
+    call without a workspace (bitwise equal); rows of the split ones pass through the
+    merge and match the oracle to the bf16 tolerance."""
+    note(f"case partial split {q_len}x{kv_len}")
+    f = plan_fields(q_len, kv_len)
+    assert int(f["segments"]) == nseg and int(f["whole_token_blocks"]) == whole
+    q0 = 32 * whole
+    q, k, v, _ = make_qkv(q_len, kv_len, seed=5700 + q_len)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ws = torch.empty(gqa.gqa_attn_prefill_workspace_size(q_len, kv_len), dtype=torch.uint8, device=DEV)
+    assert ws.numel() == nseg * (q_len - q0) * 24 * 258 * 4
+    a = gqa.gqa_attn_prefill_ws(qd, kd, vd, workspace=ws)
+    b = gqa.gqa_attn_prefill(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(a[:q0], b[:q0])
+    rows = region_rows(q_len, q0, seed=q_len)
+    mx, mean = errors(a[torch.from_numpy(rows).to(DEV)], oracle.attention(q, k, v, rows=rows))
+    note(f"  {nseg} segments from token {q0}, {len(rows)} rows: max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+    # the split rows stay within rounding of the unsplit call's
+    assert (a[q0:].float() - b[q0:].float()).abs().max().item() <= 2e-2
+
+
+def test_partial_split_int8k():
+    q_len, kv_len = 3072, 8192
+    note(f"case partial split int8k {q_len}x{kv_len}")
+    f = plan_fields(q_len, kv_len, int8k=True)
+    assert int(f["segments"]) == 2 and int(f["whole_token_blocks"]) == 64
+    q0 = 32 * 64
+    q, k, v, _ = make_qkv(q_len, kv_len, seed=5800)
+    kq, ks = oracle.quantize_rows_int8(k)
+    args = (q.to(DEV), torch.from_numpy(kq).to(DEV), v.to(DEV))
+    a = gqa.gqa_attn_prefill_ws(*args, k_scale=torch.from_numpy(ks).to(DEV))
+    b = gqa.gqa_attn_prefill(*args, k_scale=torch.from_numpy(ks).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(a[:q0], b[:q0])
+    rows = region_rows(q_len, q0, seed=7)
+    ref = oracle.attention_int8k(q, kq, ks, v, rows=rows)
+    e = np.abs(a[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64) - ref)
+    note(f"  {len(rows)} rows: max {e.max():.3e}")
+    assert e.max() <= 2e-3
