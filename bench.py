@@ -52,8 +52,15 @@ def parse():
 
 
 def source_digest() -> str:
+    """sha256[:16] of the kernel source followed by the hipcc flags it is built with
+    (a flag change changes the kernel as much as a source change)."""
+    from gqa_causal_prefill_amd.build import HIPCC_FLAGS
+
+    h = hashlib.sha256()
     with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        h.update(f.read())
+    h.update(" ".join(HIPCC_FLAGS).encode())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload_name: str):
@@ -64,7 +71,7 @@ def load_traffic(workload_name: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != source_digest():
+    if rec.get("kernel_build_sha256_16") != source_digest():
         return None
     return rec.get("hbm_bytes_per_launch")
 

@@ -29,6 +29,10 @@ QB2_LIB = os.path.join(PKG, "libgqa_prefill_qb2.so")
 #   instructions, which cannot address AGPRs; in the AGPR form the compiler moves
 #   each one (and, short of AGPRs, part of the output accumulator) between the two
 #   files on every tile.
+# -amdgpu-sched-strategy=max-ilp: the machine scheduler favours instruction-level
+#   parallelism over register pressure (the kernel runs one wave per SIMD at any
+#   register count). Measured 1.5% faster on the bf16 prefill loop, neutral with INT8
+#   keys.
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
@@ -37,6 +41,7 @@ HIPCC_FLAGS = [
     "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    "-mllvm", "-amdgpu-sched-strategy=max-ilp",
 ]
 
 
