@@ -29,6 +29,9 @@ METRIC = "GQA causal prefill attn TFLOP/s + % MFMA peak, q4096×kv32K, 24Q/4KV d
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk (the published 2.5 PFLOP/s dense)
 PEAK_INT8_TOPS = 5033.2
 HQ, HKV, D = 24, 4, 256
+# The MI355X raises its clock over roughly the first 100 ms of sustained load: a 4096 x
+# 4096 launch took 0.222 ms in a burst of 30 and 0.177 ms after 600 back-to-back launches.
+WARMUP_SECONDS = 0.3
 KERNEL_SOURCE = os.path.join(ROOT, "gqa_causal_prefill_amd", "csrc", "gqa_prefill.hip")
 
 
@@ -36,7 +39,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least 20, and enough for about "
+                         f"{WARMUP_SECONDS} s of GPU work, so the clock has settled)")
     ap.add_argument("--workload", type=int, default=3,
                     help="1 tiny, 2 4096x8192, 3 4096x32768 (default), 4 paged 512x32768, "
                          "5 int8-k 3072x16384, 6 4096x16384, 7 paged int8-k 512x32768, "
@@ -160,8 +165,22 @@ def main():
         torch.cuda.synchronize()
         print(f"bench: copied {n} bytes twice for counter calibration", file=sys.stderr, flush=True)
         del src, dst
+    done = 0   # warm-up steps run so far
+    if args.warmup is None:
+        # the first 4 warm-up steps also time the step; then warm up for WARMUP_SECONDS
+        # of work in all (at least 20 steps)
+        probe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        step()
+        probe[0].record(stream)
+        for _ in range(3):
+            step()
+        probe[1].record(stream)
+        torch.cuda.synchronize()
+        done = 4
+        per_step = probe[0].elapsed_time(probe[1]) / 3 / 1e3
+        args.warmup = max(20, int(WARMUP_SECONDS / max(per_step, 1e-6)))
     print(f"bench: {w.name} warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    for _ in range(args.warmup - done):
         step()
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
