@@ -113,10 +113,15 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v,
  * Long histories may be cut into KV segments, as the pages do for decode attention
  * and for chunked prefill with history ("gfx936 DCU上实现INT8 QK MMAC" §4): this
  * happens when one workgroup per (KV head, 32 query tokens) would leave compute
- * units idle (fewer workgroups than CUs; the segment count comes from an estimate of
- * the launch's run time). Each segment then
+ * units idle. With fewer workgroups than CUs every (KV head, token block) is cut the
+ * same way; a larger grid whose last round of workgroups would leave CUs idle has only
+ * its longest token blocks (the last query tokens) cut, into as many segments as make
+ * the work a whole number of rounds. Either choice comes from an estimate of the
+ * launch's run time and is taken only for a clear gain. Each segment then
  * writes its unnormalised output, its per-row reference maximum and row sum to the
- * workspace, and a merge step combines them by the log-sum-exp rule into `out`.
+ * workspace, and a merge step combines them by the log-sum-exp rule into `out`; the
+ * rows of token blocks that are not cut are written directly. The workspace holds
+ * segments x (rows of the cut token blocks) x 24 x (256 + 2) floats.
  * With INT8 keys every segment quantises its query rows itself (same codes).
  *
  * paged, int8k: 0 or 1. Pure host function. Returns 0 for arguments
@@ -192,7 +197,8 @@ int gqa_quantize_rows_int8(const void* x, int64_t rows, void* xq, float* scale,
 /*
  * gqa_attn_prefill_plan - the launch gqa_attn_prefill_ws would choose for a call
  * with these lengths (variant name, workgroup count, threads per workgroup,
- * bytes of LDS, KV segments, workspace bytes), written as text into buf (at most
+ * bytes of LDS, KV segments, token blocks run whole, workspace bytes), written as
+ * text into buf (at most
  * n bytes, NUL-terminated). gqa_attn_prefill makes the same choice with one
  * segment.
  * Pure host function: touches no device. The variant depends on the lengths

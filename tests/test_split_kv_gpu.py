@@ -211,3 +211,25 @@ def test_partial_split_int8k():
     e = np.abs(a[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64) - ref)
     note(f"  {len(rows)} rows: max {e.max():.3e}")
     assert e.max() <= 2e-3
+
+
+def test_partial_split_restart():
+    """Keys from 2000 on score 144 (log2 units) above the first tile: every whole token
+    block and the first segment of every cut one restarts with exact maxima; the second
+    segments take a high reference from their first tile; the merge weighs each cut
+    block's segments together."""
+    q_len, kv_len, start = 3072, 8192, 2000
+    note(f"case partial split restart {q_len}x{kv_len}")
+    f = plan_fields(q_len, kv_len)
+    assert int(f["segments"]) == 2 and int(f["whole_token_blocks"]) == 64
+    q, k, v, _ = make_qkv(q_len, kv_len, seed=5900)
+    q2, k2 = q.to(torch.float32).clone(), k.to(torch.float32).clone()
+    q2[..., 0] += 40.0
+    k2[start:, :, 0] = 40.0
+    q, k = q2.to(torch.bfloat16), k2.to(torch.bfloat16)
+    out = gqa.gqa_attn_prefill_ws(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    rows = region_rows(q_len, 32 * 64, seed=11)
+    mx, mean = errors(out[torch.from_numpy(rows).to(DEV)], oracle.attention(q, k, v, rows=rows))
+    note(f"  {len(rows)} rows: max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
