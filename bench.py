@@ -47,6 +47,10 @@ def parse():
                          "5 int8-k 3072x16384, 6 4096x16384, 7 paged int8-k 512x32768, "
                          "8 decode 1x32768, 9 paged decode 1x32768, "
                          "10 paged int8-k decode 1x32768")
+    ap.add_argument("--query-block", type=int, default=3, choices=(3, 2),
+                    help="query columns per wave in 16-column blocks: 3 (the library: a "
+                         "workgroup is 32 tokens x the 6 heads of a KV head) or 2 (the second "
+                         "build: 64 tokens x 2 heads), for comparing the two shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="query rows of the workload the CPU oracle computes (all 24 heads)")
@@ -122,7 +126,11 @@ def main():
     import torch
 
     import gqa_causal_prefill_amd as gqa
+    from gqa_causal_prefill_amd import binding as gqa_binding, build as gqa_build
     from gqa_synth import WORKLOADS, make_workload
+
+    if args.query_block == 2:
+        gqa_binding.LIB = gqa_build.QB2_LIB   # before the library is first loaded
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -200,11 +208,13 @@ def main():
     alg_bytes = (2 * w.q_len * HQ * D * 2 + kv_rows * D * (1 if w.int8k else 2)
                  + kv_rows * D * 2 + (kv_rows * 4 if w.int8k else 0)
                  + (4 * ((w.kv_len + 15) // 16) if w.paged else 0))
+    # the committed counter records are of the default build (query block 3)
+    traffic = load_traffic(w.name) if args.query_block == 3 else None
     if flops / alg_bytes < 315.0:
         # below the ridge (2516.6 TFLOP/s / 8 TB/s): a decode-sized chunk is HBM-bound
         gbs = alg_bytes / (ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
-                    "frac": round(gbs / 8000.0, 4), "traffic": load_traffic(w.name)}
+                    "frac": round(gbs / 8000.0, 4), "traffic": traffic}
     if w.int8k:
         # Q·K^T on int8 MFMA, P·V on bf16 MFMA: time at peak is the sum of both halves
         t_peak = (flops / 2) / (PEAK_INT8_TOPS * 1e12) + (flops / 2) / (PEAK_BF16_TFLOPS * 1e12)
@@ -214,7 +224,7 @@ def main():
     if flops / alg_bytes >= 315.0:
         roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": round(peak, 1),
                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                    "traffic": load_traffic(w.name)}
+                    "traffic": traffic}
     rec = {
         "metric": METRIC,
         "value": round(tflops, 3),
