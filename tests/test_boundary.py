@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from gqa_causal_prefill_amd import build as gqa_build
@@ -237,3 +238,45 @@ def test_qint8_binding_checks_dtypes():
     with pytest.raises(ValueError):   # k_scale is required
         binding.gqa_attn_prefill_qint8(q, torch.zeros((4, 24)), torch.zeros((8, 4, 256),
                                        dtype=torch.int8), torch.zeros((8, 4, 256)))
+
+
+def _plan_fields(q_len, kv_len, paged=False, int8k=False):
+    plan = binding.gqa_attn_prefill_plan(q_len, kv_len, paged=paged, int8k=int8k)
+    return {kv.split("=")[0]: kv.split("=")[1] for kv in plan.split()}
+
+
+def test_plan_invariants_over_many_shapes():
+    """What the kernel assumes of every plan, over a sweep of lengths: the grid holds
+    one workgroup per whole token block and `segments` per cut one; the workspace holds
+    the cut blocks' rows; every KV segment is at least 8 tiles of 64 keys long and
+    starts at or before its token block's first query (position kv_len - q_len + the
+    block's first token), so the first key of every segment is visible to every query
+    of its workgroup."""
+    rng = np.random.default_rng(0)
+    shapes = [(q, q + h) for q in (1, 3, 4, 5, 31, 32, 33, 100, 512, 1000, 2048, 2080, 2112, 3000,
+                                   3072, 4096, 5000, 6000, 8192, 9000)
+              for h in (0, 1, 500, 4096, 30000)]
+    shapes += [(int(q), int(q + h)) for q, h in zip(rng.integers(1, 12000, 60), rng.integers(0, 70000, 60))]
+    cut_shapes = 0
+    for q_len, kv_len in shapes:
+        f = _plan_fields(q_len, kv_len)
+        tok = 4 if q_len <= 4 else 32
+        n_tblk = -(-q_len // tok)
+        nseg, whole = int(f["segments"]), int(f["whole_token_blocks"])
+        wg, ws = int(f["workgroups"]), int(f["workspace_bytes"])
+        assert binding.gqa_attn_prefill_workspace_size(q_len, kv_len) == ws
+        if nseg == 1:
+            assert whole == n_tblk and wg == 4 * n_tblk and ws == 0, (q_len, kv_len, f)
+            continue
+        cut_shapes += 1
+        assert 0 <= whole < n_tblk, (q_len, kv_len, f)
+        assert wg == 4 * (whole + (n_tblk - whole) * nseg), (q_len, kv_len, f)
+        assert ws == nseg * (q_len - tok * whole) * 24 * 258 * 4, (q_len, kv_len, f)
+        off = kv_len - q_len
+        for t in range(whole, n_tblk):
+            last = min((t + 1) * tok, q_len)
+            tiles = (off + last + 63) // 64
+            starts = [tiles * s // nseg for s in range(nseg + 1)]
+            assert min(b - a for a, b in zip(starts, starts[1:])) >= 8, (q_len, kv_len, t, f)
+            assert starts[-2] * 64 <= off + t * tok, (q_len, kv_len, t, f)
+    assert cut_shapes >= 20
