@@ -46,7 +46,8 @@ def parse():
                     help="1 tiny, 2 4096x8192, 3 4096x32768 (default), 4 paged 512x32768, "
                          "5 int8-k 3072x16384, 6 4096x16384, 7 paged int8-k 512x32768, "
                          "8 decode 1x32768, 9 paged decode 1x32768, "
-                         "10 paged int8-k decode 1x32768")
+                         "10 paged int8-k decode 1x32768, "
+                         "11 3072x16384 with bf16 keys (workload 5's inputs)")
     ap.add_argument("--query-block", type=int, default=3, choices=(3, 2),
                     help="query columns per wave in 16-column blocks: 3 (the library: a "
                          "workgroup is 32 tokens x the 6 heads of a KV head) or 2 (the second "

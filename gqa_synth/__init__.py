@@ -68,6 +68,8 @@ WORKLOADS = {
     9: Workload("decode_paged_1x32768", 1, 32768, paged=True, num_blocks=2048, seed=9),
     10: Workload("decode_paged_int8k_1x32768", 1, 32768, paged=True, int8k=True, num_blocks=2048,
                  seed=10),
+    # the INT8-K chunk's shape and inputs (seed 5) with bf16 keys: what INT8 keys save
+    11: Workload("bf16k_3072x16384", 3072, 16384, seed=5),
 }
 
 

@@ -204,6 +204,24 @@ def test_full_size_contiguous_sampled(idx):
     assert mx <= BF16_MAX and mean <= BF16_MEAN
 
 
+def test_full_size_bf16_partial_split_sampled():
+    """The INT8-K chunk's shape with bf16 keys, in the launch configuration the
+    benchmark times: its 32 longest token blocks cut into 2 KV segments."""
+    w = WORKLOADS[11]
+    note(f"case {w.name}: generating inputs")
+    d = make_workload(w)
+    plan = gqa.gqa_attn_prefill_plan(w.q_len, w.kv_len)
+    assert "segments=2 whole_token_blocks=64" in plan
+    note(f"case {w.name}: running")
+    out = gqa.gqa_attn_prefill_ws(d["q"].to(DEV), d["k"].to(DEV), d["v"].to(DEV))
+    torch.cuda.synchronize()
+    rows = sample_rows(w.q_len, seed=11)
+    ref = oracle.attention(d["q"], d["k"], d["v"], rows=rows)
+    mx, mean = errors(out[torch.from_numpy(rows).to(DEV)], ref)
+    note(f"  {len(rows)} rows: max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
 def test_full_size_paged_sampled():
     w = WORKLOADS[4]
     note(f"case {w.name}: generating inputs")
