@@ -112,7 +112,6 @@ struct Params {
   float* ws_ml;            // n_seg > 1: (reference maximum, row sum) [n_seg, split rows, 24, 2]
 };
 
-
 // Workgroup shape for QB 16-column query blocks per wave. QB = 3 and QB = 2 map a
 // column to a token (16-token runs) and a block to a query head. QB = 1 is the decode
 // shape: one token per wave, and column c of its single block is query head 6 g + c of
@@ -598,9 +597,10 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   const int tw = w % S::kTokenBlocks;
   const int hw = w / S::kTokenBlocks;
 
-  // Workgroup id -> (KV head, KV segment, head subset, token block). id % 4 is the KV
-  // head, so workgroups dispatched round-robin over the 8 XCDs keep one KV head per
-  // XCD (its K/V stream shares that XCD's L2); token blocks go longest first.
+  // Workgroup id -> (KV head, KV segment, head subset, token block) by unit_of. id % 4 is
+  // the KV head, so workgroups dispatched round-robin over the 8 XCDs keep one KV head per
+  // XCD (its K/V stream shares that XCD's L2); whole token blocks go longest first, then
+  // the segments of the cut ones.
   const Unit unit = unit_of<QB>(p, blockIdx.x);
   const int g = unit.g;
   const int seg = unit.seg;
