@@ -233,3 +233,36 @@ def test_partial_split_restart():
     mx, mean = errors(out[torch.from_numpy(rows).to(DEV)], oracle.attention(q, k, v, rows=rows))
     note(f"  {len(rows)} rows: max {mx:.3e} mean {mean:.3e}")
     assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+def test_partial_split_paged_bitwise_equal_to_contiguous():
+    """A partially split grid over paged caches (bf16, and INT8 keys in the split-d page
+    layout) runs the same arithmetic as over contiguous K/V: the outputs are bitwise
+    equal, whole token blocks and cut ones alike."""
+    from gqa_synth import scatter_paged_int8_splitd, scatter_paged_scales
+
+    q_len, kv_len, nb = 3072, 8192, 600
+    note(f"case partial split paged {q_len}x{kv_len}")
+    for int8k in (False, True):
+        f = plan_fields(q_len, kv_len, paged=True, int8k=int8k)
+        assert int(f["segments"]) == 2 and int(f["whole_token_blocks"]) == 64, f
+    q, k, v, rng = make_qkv(q_len, kv_len, seed=6000)
+    bt = block_table_for(rng, kv_len, nb)
+    qd, btd = q.to(DEV), bt.to(DEV)
+    vc = scatter_paged(v, bt, nb).to(DEV)
+    a = gqa.gqa_attn_prefill_ws(qd, scatter_paged(k, bt, nb).to(DEV), vc, block_table=btd,
+                                kv_len=kv_len)
+    b = gqa.gqa_attn_prefill_ws(qd, k.to(DEV), v.to(DEV))
+    kq, ks = oracle.quantize_rows_int8(k)
+    kq_t, ks_t = torch.from_numpy(kq), torch.from_numpy(ks)
+    c = gqa.gqa_attn_prefill_ws(qd, scatter_paged_int8_splitd(kq_t, bt, nb).to(DEV), vc,
+                                block_table=btd, kv_len=kv_len,
+                                k_scale=scatter_paged_scales(ks_t, bt, nb).to(DEV))
+    d = gqa.gqa_attn_prefill_ws(qd, kq_t.to(DEV), v.to(DEV), k_scale=ks_t.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(c, d)
+    rows = region_rows(q_len, 32 * 64, seed=13)
+    mx, mean = errors(a[torch.from_numpy(rows).to(DEV)], oracle.attention(q, k, v, rows=rows))
+    note(f"  bf16 {len(rows)} rows: max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
