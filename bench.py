@@ -52,6 +52,10 @@ def parse():
                     help="query columns per wave in 16-column blocks: 3 (the library: a "
                          "workgroup is 32 tokens x the 6 heads of a KV head) or 2 (the second "
                          "build: 64 tokens x 2 heads), for comparing the two shapes")
+    ap.add_argument("--q-len", type=int, default=None,
+                    help="run the workload's kind (contiguous only) at this q_len instead")
+    ap.add_argument("--kv-len", type=int, default=None,
+                    help="run the workload's kind (contiguous only) at this kv_len instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="query rows of the workload the CPU oracle computes (all 24 heads)")
@@ -134,6 +138,19 @@ def main():
         gqa_binding.LIB = gqa_build.QB2_LIB   # before the library is first loaded
 
     w = WORKLOADS[args.workload]
+    if args.q_len is not None or args.kv_len is not None:
+        if w.paged:
+            print(json.dumps({"error": "--q-len / --kv-len take a contiguous workload"}))
+            sys.exit(2)
+        import dataclasses
+
+        q_len = w.q_len if args.q_len is None else args.q_len
+        kv_len = w.kv_len if args.kv_len is None else args.kv_len
+        if not 0 < q_len <= kv_len:
+            print(json.dumps({"error": "need 0 < q_len <= kv_len"}))
+            sys.exit(2)
+        kind = "int8k" if w.int8k else "bf16"
+        w = dataclasses.replace(w, name=f"{kind}_{q_len}x{kv_len}", q_len=q_len, kv_len=kv_len)
     dev = torch.device("cuda:0")
     print(f"bench: {w.name} generating inputs", file=sys.stderr, flush=True)
     d = make_workload(w)
