@@ -1,10 +1,13 @@
 """Parity of the KV-segment path (gqa_attn_prefill_ws) with the CPU oracle.
 
-When q_len is short the call cuts the history into KV segments, each workgroup
-writes an unnormalised partial output with its reference maximum and row sum, and a
-merge kernel combines them by the log-sum-exp rule. The result is the same softmax,
-so the bf16 tolerances of the unsplit path apply unchanged (max |err| <= 1e-2, mean
-|err| <= 1e-3 against the float64 oracle), element by element on every shape here.
+When q_len is short the call cuts every token block's history into KV segments; when
+a larger grid would end in a part-filled round of workgroups, only its longest token
+blocks are cut. Each cut workgroup writes an unnormalised partial output with its
+reference maximum and row sum, and a merge kernel combines them by the log-sum-exp
+rule. The result is the same softmax, so the bf16 tolerances of the unsplit path apply
+unchanged (max |err| <= 1e-2, mean |err| <= 1e-3 against the float64 oracle), element
+by element on the small shapes and on sampled rows of the large ones; rows of token
+blocks that are not cut are bitwise those of the call without a workspace.
 """
 
 import numpy as np
