@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--kv-len", type=int, default=None,
                     help="run the workload's kind (contiguous only) at this kv_len instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048,
+    ap.add_argument("--cpu-rows", type=int, default=3072,
                     help="query rows of the workload the CPU oracle computes (all 24 heads)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before warm-up, run a plain device copy of MIB MiB (for scaling "
