@@ -99,10 +99,23 @@ def gqa_attn_prefill_workspace_size(q_len: int, kv_len: int, paged: bool = False
     return int(library().gqa_attn_prefill_workspace_size(q_len, kv_len, int(paged), int(int8k)))
 
 
-def _stream_handle(t: torch.Tensor, stream):
-    if stream is None:
-        stream = torch.cuda.current_stream(t.device)
+def _launch_stream(dev, stream):
+    """The torch stream a call is enqueued on: `stream`, else torch's current stream."""
+    if dev.type != "cuda":
+        raise ValueError("the library runs on the GPU; the first tensor is on " + str(dev))
+    return torch.cuda.current_stream(dev) if stream is None else stream
+
+
+def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _alloc_on(stream, shape, dtype, dev):
+    """A tensor the binding allocates for a call on `stream`: allocated with that stream
+    current, so torch's caching allocator orders any reuse of its memory after the work
+    enqueued on `stream`, whichever stream was current when the binding was called."""
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=dev)
 
 
 def _ptr(t):
@@ -120,9 +133,10 @@ def _expect(t, name, dtype, shape, device):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out,
+def _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out, stream,
                   q_dtype=torch.bfloat16):
-    """Checks dtypes, shapes, contiguity and device; returns the C arguments and out."""
+    """Checks dtypes, shapes, contiguity and device; returns the C arguments and out
+    (allocated for `stream` when the caller passes none)."""
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("gqa_attn_prefill runs on the GPU; q is on " + str(dev))
@@ -148,7 +162,7 @@ def _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out,
         ks_shape = (nb, NUM_KV_HEADS, BLOCK_SIZE) if paged else (kv_len, NUM_KV_HEADS)
         _expect(k_scale, "k_scale", torch.float32, ks_shape, dev)
     if out is None:
-        out = torch.empty((q_len, NUM_Q_HEADS, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        out = _alloc_on(stream, (q_len, NUM_Q_HEADS, HEAD_DIM), torch.bfloat16, dev)
     else:
         _expect(out, "out", torch.bfloat16, (q_len, NUM_Q_HEADS, HEAD_DIM), dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(block_table), nb, _ptr(k_scale), q_len, kv_len,
@@ -170,8 +184,9 @@ def gqa_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     [num_blocks, 4, 16, 16, 16] and k_scale float32 [num_blocks, 4, 16].
     Returns out (bf16 [q_len, 24, 256]).
     """
-    args, out, _ = _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out)
-    st = library().gqa_attn_prefill(*args, _stream_handle(q, stream))
+    s = _launch_stream(q.device, stream)
+    args, out, _ = _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out, s)
+    st = library().gqa_attn_prefill(*args, _stream_handle(s))
     if st != GQA_OK:
         raise GqaError(st, "gqa_attn_prefill")
     return out
@@ -186,27 +201,30 @@ def gqa_attn_prefill_ws(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     gqa_attn_prefill_ws in include/gqa_prefill.h). `workspace` is a device tensor of
     at least gqa_attn_prefill_workspace_size() bytes; when it is None and the call
     splits, one is allocated through torch for this call."""
+    s = _launch_stream(q.device, stream)
     args, out, lens = _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len,
-                                    out)
-    ws_ptr, ws_bytes = _workspace_args(workspace, lens, q.device)
-    st = library().gqa_attn_prefill_ws(*args, ws_ptr, ws_bytes, _stream_handle(q, stream))
+                                    out, s)
+    ws, ws_ptr, ws_bytes = _workspace_args(workspace, lens, q.device, s)
+    st = library().gqa_attn_prefill_ws(*args, ws_ptr, ws_bytes, _stream_handle(s))
+    del ws   # held until the launch is enqueued
     if st != GQA_OK:
         raise GqaError(st, "gqa_attn_prefill_ws")
     return out
 
 
-def _workspace_args(workspace, lens, dev):
-    """(pointer, bytes) of the caller's workspace, or of one allocated through torch
-    for this call when it is None and the call splits."""
+def _workspace_args(workspace, lens, dev, stream):
+    """(tensor, pointer, bytes) of the caller's workspace, or of one allocated through
+    torch for this call on `stream` when it is None and the call splits. The caller
+    keeps the tensor referenced until the launch is enqueued."""
     if workspace is None:
         need = gqa_attn_prefill_workspace_size(*lens)
         if need > 0:
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            workspace = _alloc_on(stream, (need,), torch.uint8, dev)
     if workspace is None:
-        return None, 0
+        return None, None, 0
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on " + str(dev))
-    return _ptr(workspace), workspace.numel() * workspace.element_size()
+    return workspace, _ptr(workspace), workspace.numel() * workspace.element_size()
 
 
 def gqa_attn_prefill_qint8(q_codes: torch.Tensor, q_scale: torch.Tensor, k: torch.Tensor,
@@ -221,12 +239,14 @@ def gqa_attn_prefill_qint8(q_codes: torch.Tensor, q_scale: torch.Tensor, k: torc
     other arguments are those of gqa_attn_prefill_ws."""
     if k_scale is None:
         raise ValueError("gqa_attn_prefill_qint8 takes INT8 keys: k_scale is required")
+    s = _launch_stream(q_codes.device, stream)
     args, out, lens = _prefill_args(q_codes, k, v, block_table, num_blocks, k_scale, q_len,
-                                    kv_len, out, q_dtype=torch.int8)
+                                    kv_len, out, s, q_dtype=torch.int8)
     _expect(q_scale, "q_scale", torch.float32, (lens[0], NUM_Q_HEADS), q_codes.device)
-    ws_ptr, ws_bytes = _workspace_args(workspace, lens, q_codes.device)
+    ws, ws_ptr, ws_bytes = _workspace_args(workspace, lens, q_codes.device, s)
     st = library().gqa_attn_prefill_qint8(args[0], _ptr(q_scale), *args[1:], ws_ptr, ws_bytes,
-                                          _stream_handle(q_codes, stream))
+                                          _stream_handle(s))
+    del ws   # held until the launch is enqueued
     if st != GQA_OK:
         raise GqaError(st, "gqa_attn_prefill_qint8")
     return out
@@ -244,14 +264,15 @@ def gqa_quantize_rows_int8(x: torch.Tensor, xq: torch.Tensor | None = None,
     if x.dtype != torch.bfloat16 or x.shape[-1] != HEAD_DIM or not x.is_contiguous():
         raise ValueError("x must be a contiguous bf16 tensor [..., 256]")
     rows = x.numel() // HEAD_DIM
+    s = _launch_stream(x.device, stream)
     if xq is None:
-        xq = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+        xq = _alloc_on(s, x.shape, torch.int8, x.device)
     if scale is None:
-        scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+        scale = _alloc_on(s, x.shape[:-1], torch.float32, x.device)
     _expect(xq, "xq", torch.int8, x.shape, x.device)
     _expect(scale, "scale", torch.float32, x.shape[:-1], x.device)
     st = library().gqa_quantize_rows_int8(_ptr(x), rows, _ptr(xq), _ptr(scale),
-                                          _stream_handle(x, stream))
+                                          _stream_handle(s))
     if st != GQA_OK:
         raise GqaError(st, "gqa_quantize_rows_int8")
     return xq, scale

@@ -52,12 +52,17 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def _compile(sources, output, verbose=False, defines=()):
+def _start(sources, output, defines=()):
     cmd = [hipcc(), *HIPCC_FLAGS, *defines, f"-I{INCLUDE}", "-o", output + ".tmp", *sources]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines()
-            if "not a recognized feature" not in ln]
-    if res.returncode != 0:
+    proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    return cmd, proc, output
+
+
+def _finish(job, verbose=False):
+    cmd, proc, output = job
+    text, _ = proc.communicate()
+    msgs = [ln for ln in text.splitlines() if "not a recognized feature" not in ln]
+    if proc.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
@@ -65,10 +70,19 @@ def _compile(sources, output, verbose=False, defines=()):
 
 
 def build(verbose: bool = False) -> None:
-    """Compile the libraries (always, even if they exist)."""
-    _compile([os.path.join(CSRC, "gqa_prefill.hip")], LIB, verbose)
-    _compile([os.path.join(CSRC, "gqa_prefill.hip")], QB2_LIB, verbose, ("-DGQA_DEFAULT_QB=2",))
-    _compile([os.path.join(CSRC, "layout_probe.hip")], PROBE_LIB, verbose)
+    """Compile the libraries (always, even if they exist), the three in parallel."""
+    src = os.path.join(CSRC, "gqa_prefill.hip")
+    jobs = [_start([src], LIB),
+            _start([src], QB2_LIB, ("-DGQA_DEFAULT_QB=2",)),
+            _start([os.path.join(CSRC, "layout_probe.hip")], PROBE_LIB)]
+    errors = []
+    for job in jobs:
+        try:
+            _finish(job, verbose)
+        except RuntimeError as e:
+            errors.append(str(e))
+    if errors:
+        raise RuntimeError("\n\n".join(errors))
 
 
 if __name__ == "__main__":

@@ -17,24 +17,14 @@ import gqa_causal_prefill_amd as gqa
 import oracle
 from gqa_synth import (WORKLOADS, block_table_for, make_qkv, make_workload, scatter_paged,
                        scatter_paged_int8_splitd, scatter_paged_scales)
+from tolerance import BF16_MAX, BF16_MEAN, INT8_MAX, errors, int8_excess  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
-BF16_MAX, BF16_MEAN, INT8_MAX = 1e-2, 1e-3, 2e-3
 
 
 def note(msg):
     print(msg, flush=True)
-
-
-def errors(out, ref):
-    e = np.abs(out.float().cpu().numpy().astype(np.float64) - ref)
-    return float(e.max()), float(e.mean())
-
-
-def int8_excess(out, ref):
-    e = np.abs(out.float().cpu().numpy().astype(np.float64) - ref)
-    return float(np.max(e - (INT8_MAX + 2.0 ** -8 * np.abs(ref))))
 
 
 def decode_plan(q_len, kv_len, paged=False, int8k=False):
