@@ -9,11 +9,13 @@ library has not been built.
 from .binding import (  # noqa: F401
     BLOCK_SIZE,
     HEAD_DIM,
+    NOALLOC_SCRATCH_BYTES,
     NUM_KV_HEADS,
     NUM_Q_HEADS,
     GqaError,
     gqa_abi_version,
     gqa_attn_prefill,
+    gqa_attn_prefill_noalloc,
     gqa_attn_prefill_plan,
     gqa_attn_prefill_qint8,
     gqa_attn_prefill_workspace_size,

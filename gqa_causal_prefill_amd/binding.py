@@ -30,7 +30,10 @@ _STATUS_NAMES = {
     4: "GQA_ERR_UNSUPPORTED",
     5: "GQA_ERR_HIP",
     6: "GQA_ERR_WORKSPACE",
+    7: "GQA_ERR_SCRATCH",
 }
+# bytes of device scratch memory gqa_attn_prefill_noalloc holds per GPU
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class GqaError(RuntimeError):
@@ -63,6 +66,8 @@ def library() -> ctypes.CDLL:
         lib.gqa_attn_prefill_ws.restype = ctypes.c_int
         lib.gqa_attn_prefill_ws.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, vp,
                                             ctypes.c_size_t, vp]
+        lib.gqa_attn_prefill_noalloc.restype = ctypes.c_int
+        lib.gqa_attn_prefill_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, vp]
         lib.gqa_attn_prefill_qint8.restype = ctypes.c_int
         lib.gqa_attn_prefill_qint8.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, vp,
                                                ctypes.c_size_t, vp]
@@ -209,6 +214,24 @@ def gqa_attn_prefill_ws(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     del ws   # held until the launch is enqueued
     if st != GQA_OK:
         raise GqaError(st, "gqa_attn_prefill_ws")
+    return out
+
+
+def gqa_attn_prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                             block_table: torch.Tensor | None = None,
+                             num_blocks: int | None = None, k_scale: torch.Tensor | None = None,
+                             q_len: int | None = None, kv_len: int | None = None,
+                             out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """gqa_attn_prefill_ws with the KV-segment partials in the library's own scratch
+    memory (see gqa_attn_prefill_noalloc in include/gqa_prefill.h). `out` is required:
+    this call allocates nothing. Calls that may overlap on one GPU race."""
+    if out is None:
+        raise ValueError("gqa_attn_prefill_noalloc allocates nothing: pass out")
+    s = _launch_stream(q.device, stream)
+    args, out, _ = _prefill_args(q, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out, s)
+    st = library().gqa_attn_prefill_noalloc(*args, _stream_handle(s))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_attn_prefill_noalloc")
     return out
 
 

@@ -55,9 +55,18 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "gqa_prefill.h"
+
+// Device memory of gqa_attn_prefill_noalloc, for callers that cannot allocate: the
+// KV-segment partials (unnormalised O, reference maxima and row sums) that
+// gqa_attn_prefill_ws keeps in the caller's workspace. One copy per GPU, held for the
+// life of the process. In host code `scratch` names a host-side stand-in, never the
+// device memory: the host takes the address of each GPU's copy with
+// hipGetSymbolAddress (scratch_on) and passes that pointer to the kernels.
+static __device__ __align__(256) uint8_t scratch[GQA_NOALLOC_SCRATCH_BYTES];
 
 #ifndef GQA_DEFAULT_QB
 #define GQA_DEFAULT_QB 3
@@ -1470,12 +1479,16 @@ Launch plan_for(int32_t q_len, int32_t kv_len, bool paged, bool int8k) {
   return lc;
 }
 
+int scratch_on(hipStream_t stream, void** ptr);
+
 // Shared by the entry points; `allow_split` is false for the call without a workspace,
-// `q_scale` is set (and q holds int8 codes) only for the call with Q quantised beforehand.
+// `q_scale` is set (and q holds int8 codes) only for the call with Q quantised beforehand,
+// `noalloc` takes the workspace from the library's scratch array instead of the caller
+// (after every argument check, so a refused call touches no device).
 int prefill(const void* q, const float* q_scale, const void* k, const void* v,
             const int32_t* block_table, int32_t num_blocks, const float* k_scale, int32_t q_len,
             int32_t kv_len, void* out, void* workspace, size_t workspace_bytes, bool allow_split,
-            void* stream) {
+            void* stream, bool noalloc = false) {
   int st = check_prefill_lengths(q_len, kv_len);
   if (st != GQA_OK) return st;
   if (q_len == 0) return GQA_OK;
@@ -1495,6 +1508,12 @@ int prefill(const void* q, const float* q_scale, const void* k, const void* v,
   const SegPlan sp = allow_split ? segments_for(q_len, kv_len, lc) : SegPlan{};
   const int n_seg = sp.n_seg;
   const size_t ws_need = workspace_bytes_for(q_len, lc, sp);
+  if (noalloc && n_seg > 1) {
+    if (ws_need > (size_t)GQA_NOALLOC_SCRATCH_BYTES) return GQA_ERR_SCRATCH;
+    st = scratch_on(static_cast<hipStream_t>(stream), &workspace);
+    if (st != GQA_OK) return st;
+    workspace_bytes = GQA_NOALLOC_SCRATCH_BYTES;
+  }
   if (n_seg > 1) {
     if (workspace == nullptr || workspace_bytes < ws_need) return GQA_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return GQA_ERR_MISALIGNED;
@@ -1551,6 +1570,32 @@ int prefill(const void* q, const float* q_scale, const void* k, const void* v,
   return GQA_OK;
 }
 
+// The address of the GPU's copy of `scratch` for a call on `stream` (its device; the
+// current device for the null stream). Taken once per device, with that device current,
+// and kept: the array lives as long as the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on(hipStream_t stream, void** ptr) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return GQA_ERR_HIP;
+  int dev = cur;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return GQA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return GQA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return GQA_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return GQA_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return GQA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return GQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1566,6 +1611,8 @@ const char* gqa_status_string(int status) {
     case GQA_ERR_UNSUPPORTED: return "unsupported combination of arguments";
     case GQA_ERR_HIP: return "HIP launch failed";
     case GQA_ERR_WORKSPACE: return "workspace missing or smaller than gqa_attn_prefill_workspace_size()";
+    case GQA_ERR_SCRATCH:
+      return "gqa_attn_prefill_noalloc: the call needs more than GQA_NOALLOC_SCRATCH_BYTES of scratch";
     default: return "unknown status";
   }
 }
@@ -1605,6 +1652,13 @@ int gqa_attn_prefill_ws(const void* q, const void* k, const void* v, const int32
                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
   return prefill(q, nullptr, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out, workspace,
                  workspace_bytes, true, stream);
+}
+
+int gqa_attn_prefill_noalloc(const void* q, const void* k, const void* v,
+                             const int32_t* block_table, int32_t num_blocks, const float* k_scale,
+                             int32_t q_len, int32_t kv_len, void* out, void* stream) {
+  return prefill(q, nullptr, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out, nullptr, 0,
+                 true, stream, /*noalloc=*/true);
 }
 
 int gqa_attn_prefill_qint8(const void* q_codes, const float* q_scale, const void* k, const void* v,

@@ -19,14 +19,18 @@
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller; the library
- *     keeps no reference after the call returns and allocates nothing.
+ *     keeps no reference after the call returns and allocates nothing (its one
+ *     piece of device memory is the fixed scratch array of
+ *     gqa_attn_prefill_noalloc, reserved with the library's code).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued asynchronously; the library never synchronises.
  *   - Argument errors are detected on the host before anything is enqueued
  *     and returned as a gqa_status; nothing is written in that case.
  *     GQA_ERR_HIP reports a failed launch. A device fault surfaces at the
  *     caller's next synchronisation, as usual for HIP.
- *   - Calls hold no global mutable state and are thread-safe.
+ *   - Calls hold no global mutable state and are thread-safe, except
+ *     gqa_attn_prefill_noalloc, whose calls on one GPU share that GPU's scratch
+ *     array (see there).
  *   - Fixed shape: GQA_NUM_Q_HEADS, GQA_NUM_KV_HEADS, GQA_HEAD_DIM,
  *     GQA_BLOCK_SIZE below. Layouts are row-major and contiguous.
  */
@@ -40,7 +44,7 @@
 extern "C" {
 #endif
 
-#define GQA_ABI_VERSION 3
+#define GQA_ABI_VERSION 4
 #define GQA_NUM_Q_HEADS 24
 #define GQA_NUM_KV_HEADS 4
 #define GQA_HEAD_DIM 256
@@ -48,6 +52,8 @@ extern "C" {
 /* largest accepted q_len / kv_len (keeps every device offset inside int64 and
    every grid inside HIP's limits) */
 #define GQA_MAX_LEN (1 << 24)
+/* bytes of device scratch memory gqa_attn_prefill_noalloc holds per GPU (64 MiB) */
+#define GQA_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 typedef enum gqa_status {
   GQA_OK = 0,
@@ -57,7 +63,9 @@ typedef enum gqa_status {
   GQA_ERR_MISALIGNED = 3,   /* a tensor pointer is not aligned as documented */
   GQA_ERR_UNSUPPORTED = 4,  /* a combination this library refuses (none at present) */
   GQA_ERR_HIP = 5,          /* the HIP launch failed */
-  GQA_ERR_WORKSPACE = 6     /* gqa_attn_prefill_ws: workspace NULL or too small */
+  GQA_ERR_WORKSPACE = 6,    /* gqa_attn_prefill_ws: workspace NULL or too small */
+  GQA_ERR_SCRATCH = 7       /* gqa_attn_prefill_noalloc: the call's KV segments need more
+                               than GQA_NOALLOC_SCRATCH_BYTES */
 } gqa_status;
 
 /* Version of this interface; equals GQA_ABI_VERSION of the header the library
@@ -150,6 +158,32 @@ int gqa_attn_prefill_ws(const void* q, const void* k, const void* v,
                         const float* k_scale, int32_t q_len, int32_t kv_len,
                         void* out, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/*
+ * gqa_attn_prefill_noalloc - gqa_attn_prefill_ws for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the KV-segment partials go to scratch memory the library holds,
+ * one array of GQA_NOALLOC_SCRATCH_BYTES per GPU, reserved when the library's code is
+ * loaded on that GPU and kept until the process ends. The call itself allocates and
+ * frees nothing.
+ *
+ * Arguments, layouts, status codes and result as gqa_attn_prefill_ws, whose launch
+ * plan it takes: the output is bit for bit that of gqa_attn_prefill_ws with a workspace
+ * of gqa_attn_prefill_workspace_size() bytes. When that size exceeds
+ * GQA_NOALLOC_SCRATCH_BYTES the call returns GQA_ERR_SCRATCH before touching any device
+ * (gqa_attn_prefill and gqa_attn_prefill_ws still serve such lengths). The scratch array
+ * of a GPU is that of the device `stream` belongs to (the current device for NULL); its
+ * address is taken on the first call that needs it on that device.
+ *
+ * Every call on a GPU shares that GPU's array, and nothing in it needs to start at
+ * zero: each call writes every partial it later reads. Calls whose work may overlap in
+ * time on one GPU (different streams not ordered by events, or different host threads)
+ * race on the array and give wrong results; calls in order on one stream are safe.
+ */
+int gqa_attn_prefill_noalloc(const void* q, const void* k, const void* v,
+                             const int32_t* block_table, int32_t num_blocks,
+                             const float* k_scale, int32_t q_len, int32_t kv_len,
+                             void* out, void* stream);
 
 /*
  * gqa_attn_prefill_qint8 - the INT8-key call with Q quantised beforehand.

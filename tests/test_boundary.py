@@ -14,7 +14,7 @@ from gqa_causal_prefill_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER_DIR = os.path.join(ROOT, "include")
 
-OK, NULL, BADLEN, MISALIGNED, UNSUPPORTED, HIPERR, WORKSPACE = range(7)
+OK, NULL, BADLEN, MISALIGNED, UNSUPPORTED, HIPERR, WORKSPACE, SCRATCH = range(8)
 
 
 def _have_lib():
@@ -38,6 +38,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"gqa_attn_prefill", "gqa_attn_prefill_ws", "gqa_attn_prefill_workspace_size",
             "gqa_attn_prefill_qint8", "gqa_quantize_rows_int8", "gqa_attn_prefill_plan",
+            "gqa_attn_prefill_noalloc",
             "gqa_abi_version", "gqa_status_string"} <= set(names)
     lib = ctypes.CDLL(gqa_build.LIB)
     for n in names:
@@ -53,8 +54,8 @@ def test_probe_library_loads():
 
 
 def test_abi_version_and_status_strings():
-    assert binding.gqa_abi_version() == 3
-    for s in range(7):
+    assert binding.gqa_abi_version() == 4
+    for s in range(8):
         assert binding.gqa_status_string(s)
     assert binding.gqa_status_string(99) == "unknown status"
 
@@ -280,3 +281,31 @@ def test_plan_invariants_over_many_shapes():
             assert min(b - a for a, b in zip(starts, starts[1:])) >= 8, (q_len, kv_len, t, f)
             assert starts[-2] * 64 <= off + t * tok, (q_len, kv_len, t, f)
     assert cut_shapes >= 20
+
+
+def noalloc_call(q_len, kv_len, paged=False, int8k=False):
+    lib = binding.library()
+    vp = ctypes.c_void_p
+    nb = (kv_len + 15) // 16 if paged else 0
+    return lib.gqa_attn_prefill_noalloc(vp(16), vp(16), vp(16), vp(16) if paged else None, nb,
+                                        vp(16) if int8k else None, q_len, kv_len, vp(16), None)
+
+
+def test_header_scratch_size_matches_binding():
+    text = open(os.path.join(HEADER_DIR, "gqa_prefill.h")).read()
+    m = re.search(r"#define GQA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("paged,int8k", [(False, False), (True, False), (False, True), (True, True)])
+def test_noalloc_refuses_plans_beyond_its_scratch(paged, int8k):
+    """A call whose KV segments need more than the scratch array is refused on the host,
+    before any device call (this runs without a GPU); lengths whose plan fits are not
+    refused for their size."""
+    big = (1840, 131072)
+    need = binding.gqa_attn_prefill_workspace_size(*big, paged, int8k)
+    assert need > binding.NOALLOC_SCRATCH_BYTES
+    assert noalloc_call(*big, paged, int8k) == SCRATCH
+    # argument errors still come first
+    assert noalloc_call(5, 4, paged, int8k) == BADLEN
+    assert noalloc_call(0, 4, paged, int8k) == OK
