@@ -9,8 +9,10 @@ synthetic tensors already resident in HBM when the timed region starts.
 
 Prints one JSON line: TFLOP/s counted causal-effectively (4 * 24 * 256 * the
 number of visible query/key pairs per head, divided by the time), the roofline
-of the kernel against the MI355X dense bf16 MFMA peak, and the CPU oracle timed
-on a bounded sample of the same workload as a baseline.
+of the kernel against the MI355X dense bf16 MFMA peak (with, from the committed
+rocprofv3 counter record of the same kernel build, its HBM traffic per launch, that
+traffic's rate over this run's step time against 8 TB/s, and the MFMA busy share),
+and the CPU oracle timed on a bounded sample of the same workload as a baseline.
 """
 
 from __future__ import annotations
@@ -52,6 +54,10 @@ def parse():
                     help="query columns per wave in 16-column blocks: 3 (the library: a "
                          "workgroup is 32 tokens x the 6 heads of a KV head) or 2 (the second "
                          "build: 64 tokens x 2 heads), for comparing the two shapes")
+    ap.add_argument("--library", default=None,
+                    help="load this build of the library instead (a variant from "
+                         "gqa_causal_prefill_amd.build.build_variant, for comparing a tuning "
+                         "constant; such lines carry no counter record)")
     ap.add_argument("--q-len", type=int, default=None,
                     help="run the workload's kind (contiguous only) at this q_len instead")
     ap.add_argument("--kv-len", type=int, default=None,
@@ -77,9 +83,12 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload_name: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were
-    taken on the current kernel source (else None)."""
+def load_counters(workload_name: str):
+    """The committed rocprofv3 counter record of the workload's attention kernel
+    (profiles/traffic_<workload>.json), if it was taken on the current kernel source and
+    build flags; else None. It holds the HBM bytes per launch (FETCH_SIZE + WRITE_SIZE,
+    scaled by a device copy of known size) and the MFMA busy fraction
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
     if not os.path.exists(path):
         return None
@@ -87,7 +96,13 @@ def load_traffic(workload_name: str):
         rec = json.load(f)
     if rec.get("kernel_build_sha256_16") != source_digest():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def load_traffic(workload_name: str):
+    """HBM bytes per launch from the counter record (None when it is stale or absent)."""
+    rec = load_counters(workload_name)
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(w, d, rows_n):
@@ -136,6 +151,8 @@ def main():
 
     if args.query_block == 2:
         gqa_binding.LIB = gqa_build.QB2_LIB   # before the library is first loaded
+    if args.library is not None:
+        gqa_binding.LIB = os.path.abspath(args.library)
 
     w = WORKLOADS[args.workload]
     if args.q_len is not None or args.kv_len is not None:
@@ -227,12 +244,18 @@ def main():
                  + kv_rows * D * 2 + (kv_rows * 4 if w.int8k else 0)
                  + (4 * ((w.kv_len + 15) // 16) if w.paged else 0))
     # the committed counter records are of the default build (query block 3)
-    traffic = load_traffic(w.name) if args.query_block == 3 else None
+    counters = load_counters(w.name) if args.query_block == 3 and args.library is None else None
+    traffic = None if counters is None else counters.get("hbm_bytes_per_launch")
+    # HBM rate of the counted traffic over this run's step time, and the MFMA pipe's busy
+    # share from the counter pass (both null without a current counter record)
+    hbm_gbs = None if traffic is None else round(traffic / (ms * 1e-3) / 1e9, 1)
+    mfma_busy = None if counters is None else counters.get("mfma_busy")
     if flops / alg_bytes < 315.0:
         # below the ridge (2516.6 TFLOP/s / 8 TB/s): a decode-sized chunk is HBM-bound
         gbs = alg_bytes / (ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
-                    "frac": round(gbs / 8000.0, 4), "traffic": traffic}
+                    "frac": round(gbs / 8000.0, 4), "traffic": traffic, "hbm_gbs": hbm_gbs,
+                    "mfma_busy": mfma_busy}
     if w.int8k:
         # Q·K^T on int8 MFMA, P·V on bf16 MFMA: time at peak is the sum of both halves
         t_peak = (flops / 2) / (PEAK_INT8_TOPS * 1e12) + (flops / 2) / (PEAK_BF16_TFLOPS * 1e12)
@@ -242,7 +265,7 @@ def main():
     if flops / alg_bytes >= 315.0:
         roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": round(peak, 1),
                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                    "traffic": traffic}
+                    "traffic": traffic, "hbm_gbs": hbm_gbs, "mfma_busy": mfma_busy}
     rec = {
         "metric": METRIC,
         "value": round(tflops, 3),

@@ -85,6 +85,19 @@ def build(verbose: bool = False) -> None:
         raise RuntimeError("\n\n".join(errors))
 
 
+VARIANT_DIR = os.path.join(PKG, "variants")
+
+
+def build_variant(name: str, defines) -> str:
+    """Build the library with extra preprocessor definitions (tuning constants such as
+    -DGQA_VT_DEPTH=4) as variants/libgqa_prefill_<name>.so, for comparing a tuning
+    choice with bench.py --library; returns its path. Not used by the library itself."""
+    os.makedirs(VARIANT_DIR, exist_ok=True)
+    out = os.path.join(VARIANT_DIR, f"libgqa_prefill_{name}.so")
+    _finish(_start([os.path.join(CSRC, "gqa_prefill.hip")], out, tuple(defines)))
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
     print("built", LIB, "and", PROBE_LIB)

@@ -492,7 +492,15 @@ __device__ __forceinline__ bf16x8 vt_value(const VtFrag& f) {
 // V^T fragment (ks, db) sits at vbase[db & 3] + (db >> 2) * kSegStride + ks * 4096.
 // Fragments travel in a ring of kVtDepth + 1: step N issues the reads of step
 // N + kVtDepth, then waits for its own (2 reads per step).
-constexpr int kVtDepth = 3;   // at most 2 (kVtDepth + 1) = 8 reads in flight (lgkmcnt counts to 15)
+// Depth 3 measured fastest on every cell of the pages' grid of chunk shapes against 2 and
+// 4 (the other depths are built only to compare them).
+#ifndef GQA_VT_DEPTH
+#define GQA_VT_DEPTH 3
+#endif
+constexpr int kVtDepth = GQA_VT_DEPTH;
+// at most 2 (kVtDepth + 1) reads in flight, plus the 4 key-scale reads of INT8 keys, and
+// lgkmcnt counts to 15
+static_assert(kVtDepth >= 1 && 2 * (kVtDepth + 1) + 4 <= 15, "V^T read ring depth");
 
 template <int N>
 __device__ __forceinline__ void vt_issue_step(VtFrag& f, const uint32_t (&vbase)[4]) {

@@ -38,3 +38,16 @@ def test_traffic_only_for_the_build_it_was_taken_on(monkeypatch):
     assert bench.load_traffic("longkv_4096x32768") is None
     assert bench.load_traffic("no_such_workload") is None
 
+
+
+def test_counter_record_carries_mfma_busy_for_its_build(monkeypatch):
+    """The counter record is gated like the traffic: the MFMA busy share (and the traffic
+    the HBM rate is computed from) come only from a record of the current build."""
+    path = os.path.join(ROOT, "profiles", "traffic_longkv_4096x32768.json")
+    with open(path) as f:
+        rec = json.load(f)
+    monkeypatch.setattr(bench, "source_digest", lambda: rec["kernel_build_sha256_16"])
+    got = bench.load_counters("longkv_4096x32768")
+    assert got is not None and got.get("mfma_busy") == rec.get("mfma_busy")
+    monkeypatch.setattr(bench, "source_digest", lambda: "0" * 16)
+    assert bench.load_counters("longkv_4096x32768") is None
