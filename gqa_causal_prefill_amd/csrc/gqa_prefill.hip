@@ -82,7 +82,17 @@ constexpr int kBs = GQA_BLOCK_SIZE;      // 16
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kKt = 64;                  // keys per KV tile
+// Keys per KV tile: 64 (the library). 32 is built only to compare the two (a build with
+// -DGQA_KT=32 serves contiguous K/V and refuses paged caches).
+#ifndef GQA_KT
+#define GQA_KT 64
+#endif
+constexpr int kKt = GQA_KT;              // keys per KV tile
+static_assert(kKt == 64 || kKt == 32, "KV tile of 32 or 64 keys");
+constexpr int kHalves = kKt / 32;        // 32-key halves per tile (Q·K^T units)
+constexpr int kKb = kKt / 16;            // 16-key blocks per tile (MFMA rows of S^T)
+constexpr int kWaveKeys = kKt / 4;       // keys of a tile each of the 4 waves copies
+constexpr int kPvSteps = 16 * kHalves;   // P·V steps per tile (32 keys x 16 features each)
 constexpr int kSplitBelow = 256;
 // Pass 0 restarts once a column's running sum of exponentials exceeds 2^32: every
 // exponential is then still at most 2^32 (finite in bf16 and fp32 with ample margin
@@ -91,7 +101,9 @@ constexpr int kSplitBelow = 256;
 constexpr float kOverSum = 4294967296.0f;
 constexpr float kLog2eOver16 = 1.4426950408889634f / 16.0f;
 
-constexpr int kSkTile = kKt * kHkv * 4;  // 1 KiB of key scales per tile (all KV heads)
+// key scales of a tile: a 256-byte area per wave, [KV head][16 key slots] (a 32-key tile
+// uses 8 of the 16 slots of each wave)
+constexpr int kSkTile = 4 * kHkv * 16 * 4;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -261,7 +273,7 @@ template <bool PAGED, int ROW_BYTES, bool V, bool SPLITD = false>
 struct WaveCopy {
   static_assert(!SPLITD || (PAGED && ROW_BYTES == kD), "the split-d layout is the paged INT8 K cache");
   static constexpr int kNseg = ROW_BYTES / 128;                      // 128-byte segments per row
-  static constexpr int kInsts = 2 * kNseg;                          // 8 keys x one segment each
+  static constexpr int kInsts = (kWaveKeys / 8) * kNseg;            // 8 keys x one segment each
   static constexpr int kStride = PAGED ? ROW_BYTES : kHkv * ROW_BYTES;   // bytes between keys
 
   __amdgpu_buffer_rsrc_t rsrc;
@@ -296,7 +308,7 @@ struct WaveCopy {
     const int nrec = __builtin_amdgcn_readfirstlane(bytes);
     const uint8_t* wb;
     if constexpr (PAGED) {
-      wb = base + (size_t)(blk * kHkv + g) * kBs * ROW_BYTES;
+      wb = base + (size_t)(blk * kHkv + g) * kBs * ROW_BYTES + (SPLITD ? 0 : (first & (kBs - 1)) * ROW_BYTES);
     } else {
       (void)blk;
       wb = base + ((size_t)first * kHkv + g) * ROW_BYTES;   // not dereferenced when n == 0
@@ -338,7 +350,7 @@ struct ScaleCopy {
       return (uint32_t)((lane & 15) * kHkv * 4 + (lane >> 4) * 4);
   }
   __device__ __forceinline__ ScaleCopy(const Params& p, int first, int blk, uint32_t lds_block) {
-    n = __builtin_amdgcn_readfirstlane(min(max(p.kv_len - first, 0), 16));
+    n = __builtin_amdgcn_readfirstlane(min(max(p.kv_len - first, 0), kWaveKeys));
     const uint8_t* wb;
     int bytes;
     if constexpr (PAGED) {
@@ -432,7 +444,7 @@ __device__ __forceinline__ void lds_wait2(u32x4& a, u32x4& b) {
 template <bool INT8K, int QB, bool PM, int KB0, int S, class Extra>
 __device__ __forceinline__ void qk_half(u32x4 (&kf)[2][2], uint32_t be, uint32_t bo,
                                         const typename QK<INT8K, QB>::Frag (&qf)[QB][QK<INT8K, QB>::kSteps],
-                                        typename QK<INT8K, QB>::Acc (&acc)[QB][4], Extra&& extra) {
+                                        typename QK<INT8K, QB>::Acc (&acc)[QB][kKb], Extra&& extra) {
   using Q = QK<INT8K, QB, PM>;
   if constexpr (S + 1 < Q::kSteps) {
     Q::template issue<S + 1, KB0>(kf[(S + 1) & 1], be, bo);
@@ -453,7 +465,7 @@ __device__ __forceinline__ void qk_half(u32x4 (&kf)[2][2], uint32_t be, uint32_t
 template <bool INT8K, int QB, bool PM, int KB0, class Extra>
 __device__ __forceinline__ void qk_pair(uint32_t kbuf, int kb_even, int kb_odd,
                                         const typename QK<INT8K, QB>::Frag (&qf)[QB][QK<INT8K, QB>::kSteps],
-                                        typename QK<INT8K, QB>::Acc (&acc)[QB][4], Extra&& extra) {
+                                        typename QK<INT8K, QB>::Acc (&acc)[QB][kKb], Extra&& extra) {
   using Q = QK<INT8K, QB, PM>;
   u32x4 kf[2][2];
   Q::template issue<0, KB0>(kf[0], kbuf + kb_even, kbuf + kb_odd);
@@ -555,8 +567,8 @@ struct PvStep {
                                              f32x4 (&lacc)[QB], Extra&& extra) {
     constexpr int ks = N >> 4, db = N & 15;
     extra(std::integral_constant<int, N>{});
-    constexpr int kAhead = (32 - 1 - N) < kVtDepth ? (32 - 1 - N) : kVtDepth;  // steps in flight after N
-    if constexpr (N + kVtDepth < 32) vt_issue_step<N + kVtDepth>(vf[(N + kVtDepth) % (kVtDepth + 1)], vbase);
+    constexpr int kAhead = (kPvSteps - 1 - N) < kVtDepth ? (kPvSteps - 1 - N) : kVtDepth;  // steps in flight after N
+    if constexpr (N + kVtDepth < kPvSteps) vt_issue_step<N + kVtDepth>(vf[(N + kVtDepth) % (kVtDepth + 1)], vbase);
     vt_wait<2 * kAhead>(vf[N % (kVtDepth + 1)]);
     const bf16x8 v = vt_value(vf[N % (kVtDepth + 1)]);
 #pragma unroll
@@ -573,7 +585,7 @@ struct PvStep {
           lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl[b][ks], lacc[b], 0, 0, 0);
       }
     }
-    if constexpr (N + 1 < 32) PvStep<N + 1, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc, extra);
+    if constexpr (N + 1 < kPvSteps) PvStep<N + 1, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc, extra);
   }
 };
 
@@ -660,8 +672,8 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   using VCopy = WaveCopy<PAGED, 2 * kD, true>;
   const uint32_t smem_addr = lds_addr(smem);
   const uint32_t sk_addr = smem_addr + kSkOff;   // key-scale ring (INT8 keys)
-  const uint32_t kvo[2] = {KCopy::lane_offset(lane, 0), KCopy::lane_offset(lane, 1)};
-  const uint32_t vvo[2] = {VCopy::lane_offset(lane, 0), VCopy::lane_offset(lane, 1)};
+  const uint32_t kvo[2] = {KCopy::lane_offset(lane, 0), KCopy::lane_offset(lane, kHalves - 1)};
+  const uint32_t vvo[2] = {VCopy::lane_offset(lane, 0), VCopy::lane_offset(lane, kHalves - 1)};
   const uint32_t svo = SCopy::lane_offset(lane);
   const int skey = lane & 15;   // the key whose scales this lane copies
   // Paged: the physical block of this wave's 16 keys of the tile at kbase (an entry
@@ -670,7 +682,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   // into a scalar register, which a loop-carried value can wait in until its use.
   auto block_of = [&](int kbase) -> int {
     if constexpr (PAGED) {
-      const int first = __builtin_amdgcn_readfirstlane(min(kbase + 16 * w, p.kv_len - 1));
+      const int first = __builtin_amdgcn_readfirstlane(min(kbase + kWaveKeys * w, p.kv_len - 1));
       const int entry = *(const __attribute__((address_space(4))) int32_t*)(p.bt + (first >> 4));
       return min(max(entry, 0), p.num_blocks - 1);
     } else {
@@ -679,15 +691,15 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     }
   };
   auto kcopy = [&](int kbase, int buf, int blk) {
-    return KCopy(p, p.k, g, kbase + 16 * w, blk,
-                 smem_addr + buf * kKTile + (kPM ? w * kPageBytes : 16 * w * 128));
+    return KCopy(p, p.k, g, kbase + kWaveKeys * w, blk,
+                 smem_addr + buf * kKTile + (kPM ? w * kPageBytes : kWaveKeys * w * 128));
   };
   auto vcopy = [&](int kbase, int buf, int blk) {
-    return VCopy(p, p.v, g, kbase + 16 * w, blk,
-                 smem_addr + kVOff + buf * 4 * kSegStride + 16 * w * 128);
+    return VCopy(p, p.v, g, kbase + kWaveKeys * w, blk,
+                 smem_addr + kVOff + buf * 4 * kSegStride + kWaveKeys * w * 128);
   };
   auto scopy = [&](int kbase, int slot, int blk) {
-    return SCopy(p, kbase + 16 * w, blk, sk_addr + slot * kSkTile + w * 256);
+    return SCopy(p, kbase + kWaveKeys * w, blk, sk_addr + slot * kSkTile + w * 256);
   };
   // whole-tile copies outside the pipelined loop
   auto copy_k_all = [&](int kbase, int buf, int slot) {
@@ -791,7 +803,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   f32x4 o[16][QB];
   f32x4 lacc[QB];
   float m[QB];   // reference maximum per column (log2 units), fixed during a pass
-  Acc sacc[QB][4];
+  Acc sacc[QB][kKb];
   int* const flags = reinterpret_cast<int*>(smem + kFlagOff);
 
   // S^T of the tile in K buffer `kbuf` into sacc
@@ -799,9 +811,9 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) sacc[b][kb] = Acc{0, 0, 0, 0};
+      for (int kb = 0; kb < kKb; ++kb) sacc[b][kb] = Acc{0, 0, 0, 0};
     qk_pair<INT8K, QB, kPM, 0>(kbuf, kb_even, kb_odd, qf, sacc, [](auto) {});
-    qk_pair<INT8K, QB, kPM, 2>(kbuf, kb_even, kb_odd, qf, sacc, [](auto) {});
+    if constexpr (kHalves > 1) qk_pair<INT8K, QB, kPM, 2>(kbuf, kb_even, kb_odd, qf, sacc, [](auto) {});
   };
   // INT8 keys: sacc holds int32 dot products until scale_unit turns them, in place, into
   // float scores in log2 units (their bit patterns): y = float(S) * (sK * sQ * log2(e)/16),
@@ -810,12 +822,21 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   // contraction left to the compiler), so every build rounds every score the same way.
   // The scales of keys 16 kb + 4 L .. + 3 for KV head g come from one 16-byte LDS read
   // per 16-key block kb.
+  // (32-key tiles: keys 4 L .. 4 L + 3 of block kb were copied by wave 2 kb + L / 2)
   auto sk_read = [&](uint32_t sk_slot, u32x4 (&sr)[4]) {
-    const uint32_t a = sk_slot + g * 64 + 16 * L;
-    sr[0] = lds_read_b128<0>(a);
-    sr[1] = lds_read_b128<256>(a);
-    sr[2] = lds_read_b128<512>(a);
-    sr[3] = lds_read_b128<768>(a);
+    if constexpr (kKt == 64) {
+      const uint32_t a = sk_slot + g * 64 + 16 * L;
+      sr[0] = lds_read_b128<0>(a);
+      sr[1] = lds_read_b128<256>(a);
+      sr[2] = lds_read_b128<512>(a);
+      sr[3] = lds_read_b128<768>(a);
+    } else {
+      const uint32_t a = sk_slot + g * 64 + 16 * (L & 1) + 256 * (L >> 1);
+      sr[0] = lds_read_b128<0>(a);
+      sr[1] = lds_read_b128<512>(a);
+      sr[2] = sr[0];   // unused
+      sr[3] = sr[1];
+    }
   };
   auto scale_unit = [&](auto kb_c, auto b_c, const u32x4 (&sr)[4], auto minus_m_c) {
 #pragma clang fp contract(off)
@@ -844,7 +865,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       u32x4 sr[4];
       sk_read(sk_slot, sr);
       lds_wait4<0>(sr[0], sr[1], sr[2], sr[3]);
-      static_for<0, 4 * QB>([&](auto uc) {
+      static_for<0, kKb * QB>([&](auto uc) {
         constexpr int u = decltype(uc)::value;
         scale_unit(std::integral_constant<int, u / QB>{}, std::integral_constant<int, u % QB>{}, sr,
                    std::false_type{});
@@ -858,7 +879,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
 #pragma unroll
       for (int b = 0; b < QB; ++b)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < kKb; ++kb) {
           f32x4 y = __builtin_bit_cast(f32x4, sacc[b][kb]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) y[r] = y[r] - m[b];
@@ -918,10 +939,12 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   auto tile_max = [&](int kbase, float (&mx)[QB]) {
     float sc0[QB][8], sc1[QB][8], scale[QB];
     half_scores(std::true_type{}, kbase, 0, sc0, scale);
-    half_scores(std::true_type{}, kbase, 1, sc1, scale);
+    if constexpr (kHalves > 1) half_scores(std::true_type{}, kbase, 1, sc1, scale);
 #pragma unroll
-    for (int b = 0; b < QB; ++b)
-      mx[b] = xor32_max(xor16_max(fmaxf(lane_max(sc0, b), lane_max(sc1, b)))) * scale[b];
+    for (int b = 0; b < QB; ++b) {
+      const float lm = kHalves > 1 ? fmaxf(lane_max(sc0, b), lane_max(sc1, b)) : lane_max(sc0, b);
+      mx[b] = xor32_max(xor16_max(lm)) * scale[b];
+    }
   };
 
   // Pass 0 takes each column's maximum over tile 0 as the reference (tile 0 holds key
@@ -998,7 +1021,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
         else
           scp.issue(svo, skey);
       };
-      constexpr int kSlots = 2 * Q::kSteps;   // issue slots: the K steps of both halves
+      constexpr int kSlots = kHalves * Q::kSteps;   // issue slots: the K steps of the halves
       // the copies whose slot (I * kSlots) / kCopies is SLOT
       auto copies_at = [&](auto slot_c) {
         constexpr int kSlot = decltype(slot_c)::value;
@@ -1040,7 +1063,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
         qk_pair<INT8K, QB, kPM, 2 * H>(kn, kb_even, kb_odd, qf, sacc, softmax_part);
       };
       half(std::integral_constant<int, 0>{});
-      half(std::integral_constant<int, 1>{});
+      if constexpr (kHalves > 1) half(std::integral_constant<int, 1>{});
 
       // ---- O^T += V^T(j) · P^T(j); INT8 keys: S(j+1) is scaled between the steps, where
       // the vector ALU has room (the Q·K^T halves above are short on it: half as many
@@ -1062,7 +1085,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
             // at step 1 only the 2 kVtDepth reads of steps 1 .. kVtDepth are younger
             // than the scale reads: the wait costs nothing and marks them valid
             if constexpr (N == 1) lds_wait4<2 * kVtDepth>(sr[0], sr[1], sr[2], sr[3]);
-            if constexpr (N >= 2 && N % 2 == 0 && (N - 2) / 2 < 4 * QB) {
+            if constexpr (N >= 2 && N % 2 == 0 && (N - 2) / 2 < kKb * QB) {
               constexpr int u = (N - 2) / 2;
               scale_unit(std::integral_constant<int, u / QB>{}, std::integral_constant<int, u % QB>{}, sr,
                          std::true_type{});
@@ -1307,7 +1330,8 @@ Launch shape_launch(int32_t q_len, bool int8k) {
 }
 
 constexpr int kCUs = 256;        // compute units of an MI355X
-constexpr int kMinSegTiles = 8;  // shortest KV segment (512 keys)
+constexpr int kMinSegTiles = 512 / kKt;  // shortest KV segment (512 keys)
+constexpr double kTileSeconds = 2.4e-6 * kKt / 64;   // about one workgroup's time per tile
 
 // Estimated run time, in tile times (one workgroup through one 64-key tile), of a launch
 // that cuts every (KV head, token block) into n_seg KV segments. The workgroups run
@@ -1326,7 +1350,7 @@ double plan_cost(int32_t q_len, int32_t kv_len, int tok, int n_tblk, int n_seg) 
     const int64_t T = ((int64_t)kv_len - q_len + last + kKt - 1) / kKt;
     t += (double)((T + n_seg - 1) / n_seg) + kWgTiles;
   }
-  if (n_seg > 1) t += 2.0 * n_seg * (double)q_len * kHq * (kD + 2) * 4 / (5e12 * 2.4e-6);
+  if (n_seg > 1) t += 2.0 * n_seg * (double)q_len * kHq * (kD + 2) * 4 / (5e12 * kTileSeconds);
   return t;
 }
 
@@ -1397,7 +1421,7 @@ double plan_makespan(int32_t q_len, int32_t kv_len, const Launch& lc, const SegP
           place((double)(T * (sg + 1) / sp.n_seg - T * sg / sp.n_seg));
     }
     const int64_t split_rows = (int64_t)q_len - (int64_t)sp.n_plain * tok;
-    span += 2.0 * sp.n_seg * (double)split_rows * kHq * (kD + 2) * 4 / (5e12 * 2.4e-6);
+    span += 2.0 * sp.n_seg * (double)split_rows * kHq * (kD + 2) * 4 / (5e12 * kTileSeconds);
   }
   return span;
 }
@@ -1476,13 +1500,18 @@ Launch plan_for(int32_t q_len, int32_t kv_len, bool paged, bool int8k) {
   (void)kv_len;
   const bool dec = q_len <= kDecodeMaxQ;
   Launch lc = dec ? shape_launch<1>(q_len, int8k) : shape_launch<kDefaultQB>(q_len, int8k);
+#define GQA_KT_NAME_(x) "_kt" #x
+#define GQA_KT_NAME(x) GQA_KT_NAME_(x)
   static const char* const kNames[4][3] = {
       // decode, 32 tokens x 6 heads, 64 tokens x 2 heads
-      {"bf16_contiguous_decode_t4h6_kt64", "bf16_contiguous_t32h6_kt64", "bf16_contiguous_t64h2_kt64"},
-      {"bf16_paged_decode_t4h6_kt64", "bf16_paged_t32h6_kt64", "bf16_paged_t64h2_kt64"},
-      {"int8k_contiguous_decode_t4h6_kt64", "int8k_contiguous_t32h6_kt64", "int8k_contiguous_t64h2_kt64"},
-      {"int8k_paged_splitd_decode_t4h6_kt64", "int8k_paged_splitd_t32h6_kt64",
-       "int8k_paged_splitd_t64h2_kt64"}};
+      {"bf16_contiguous_decode_t4h6" GQA_KT_NAME(GQA_KT), "bf16_contiguous_t32h6" GQA_KT_NAME(GQA_KT),
+       "bf16_contiguous_t64h2" GQA_KT_NAME(GQA_KT)},
+      {"bf16_paged_decode_t4h6" GQA_KT_NAME(GQA_KT), "bf16_paged_t32h6" GQA_KT_NAME(GQA_KT),
+       "bf16_paged_t64h2" GQA_KT_NAME(GQA_KT)},
+      {"int8k_contiguous_decode_t4h6" GQA_KT_NAME(GQA_KT), "int8k_contiguous_t32h6" GQA_KT_NAME(GQA_KT),
+       "int8k_contiguous_t64h2" GQA_KT_NAME(GQA_KT)},
+      {"int8k_paged_splitd_decode_t4h6" GQA_KT_NAME(GQA_KT), "int8k_paged_splitd_t32h6" GQA_KT_NAME(GQA_KT),
+       "int8k_paged_splitd_t64h2" GQA_KT_NAME(GQA_KT)}};
   lc.name = kNames[(int8k ? 2 : 0) + (paged ? 1 : 0)][dec ? 0 : (lc.qb == 3 ? 1 : 2)];
   return lc;
 }
@@ -1506,6 +1535,7 @@ int prefill(const void* q, const float* q_scale, const void* k, const void* v,
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
     return GQA_ERR_MISALIGNED;
   if (paged && !aligned(block_table, 4)) return GQA_ERR_MISALIGNED;
+  if (kKt != 64 && paged && int8k) return GQA_ERR_UNSUPPORTED;   // page-major INT8 tiles are 64 keys
   if (int8k && !aligned(k_scale, 4)) return GQA_ERR_MISALIGNED;
   if (q_scale != nullptr && !aligned(q_scale, 4)) return GQA_ERR_MISALIGNED;
   if (paged) {

@@ -61,7 +61,8 @@ typedef enum gqa_status {
   GQA_ERR_BAD_LENGTH = 2,   /* q_len < 0, kv_len < q_len, a length above GQA_MAX_LEN,
                                rows < 0, or num_blocks too small for kv_len */
   GQA_ERR_MISALIGNED = 3,   /* a tensor pointer is not aligned as documented */
-  GQA_ERR_UNSUPPORTED = 4,  /* a combination this library refuses (none at present) */
+  GQA_ERR_UNSUPPORTED = 4,  /* a combination this build refuses: none in the library; a
+                               comparison build with 32-key tiles refuses paged INT8 keys */
   GQA_ERR_HIP = 5,          /* the HIP launch failed */
   GQA_ERR_WORKSPACE = 6,    /* gqa_attn_prefill_ws: workspace NULL or too small */
   GQA_ERR_SCRATCH = 7       /* gqa_attn_prefill_noalloc: the call's KV segments need more
