@@ -16,7 +16,9 @@ Pages cited (by title and section; the code restates them, it copies nothing):
   quantisation Q ≈ Qq·sQ, K ≈ Kq·sK and the post-scale applied per score
   before softmax; §2.1 the [-127, 127] range and the INT32 bound; §3 the paged
   K cache walk (block table -> physical block -> slot); §4 the per-row
-  quantiser sQ = max|Q|/127, Qq = round(Q/sQ); §5.2 the GQA map kv = head/6.
+  quantiser sQ = max|Q|/127, Qq = round(Q/sQ); §5.2 the GQA map kv = head/6;
+  §6 names INT8 PV (V in INT8) and defines nothing more: ``int8pv`` states the
+  reading taken for it.
 
 Everything here is float64 unless a page fixes another precision. The one
 place that is not float64 is the INT8 quantiser, which runs in float32 (the
@@ -25,7 +27,7 @@ division and round-half-to-even), so that both sides of a comparison take the
 same integer decisions.
 
 Pin status: every function here is pinned by the CPU tests in
-``tests/test_oracle.py`` (brute force, closed forms, invariants, a library
+``tests/test_oracle.py`` and ``tests/test_oracle_int8pv.py`` (brute force, closed forms, invariants, a library
 reduction and hand-derived fixtures under ``tests/golden/``). None is
 "parity unpinned".
 """
@@ -48,4 +50,11 @@ from .prefill import (  # noqa: F401
     quantize_rows_int8,
     score_matrix,
     score_matrix_int8k,
+)
+from .int8pv import (  # noqa: F401
+    P_LEVELS,
+    attention_int8kv,
+    attention_int8qkv,
+    p_codes,
+    quantize_v_int8,
 )
