@@ -49,7 +49,8 @@ def parse():
                          "5 int8-k 3072x16384, 6 4096x16384, 7 paged int8-k 512x32768, "
                          "8 decode 1x32768, 9 paged decode 1x32768, "
                          "10 paged int8-k decode 1x32768, "
-                         "11 3072x16384 with bf16 keys (workload 5's inputs)")
+                         "11 3072x16384 with bf16 keys (workload 5's inputs), "
+                         "12 3072x16384 with INT8 keys and values (workload 5's inputs)")
     ap.add_argument("--query-block", type=int, default=3, choices=(3, 2),
                     help="query columns per wave in 16-column blocks: 3 (the library: a "
                          "workgroup is 32 tokens x the 6 heads of a KV head) or 2 (the second "
@@ -120,7 +121,11 @@ def cpu_baseline(w, d, rows_n):
     pairs = int(np.sum(off + rows + 1))
     flops = 4.0 * HQ * D * pairs
     t = time.perf_counter()
-    if w.int8k:
+    if w.int8v:
+        kq, ks = oracle.quantize_rows_int8(d["k"])
+        vq, vs = oracle.quantize_v_int8(d["v"])
+        oracle.attention_int8kv(d["q"], kq, ks, vq, vs, rows=rows)
+    elif w.int8k:
         kq, ks = oracle.quantize_rows_int8(d["k"])
         oracle.attention_int8k(d["q"], kq, ks, d["v"], rows=rows)
     else:
@@ -166,7 +171,7 @@ def main():
         if not 0 < q_len <= kv_len:
             print(json.dumps({"error": "need 0 < q_len <= kv_len"}))
             sys.exit(2)
-        kind = "int8k" if w.int8k else "bf16"
+        kind = "int8kv" if w.int8v else ("int8k" if w.int8k else "bf16")
         w = dataclasses.replace(w, name=f"{kind}_{q_len}x{kv_len}", q_len=q_len, kv_len=kv_len)
     dev = torch.device("cuda:0")
     print(f"bench: {w.name} generating inputs", file=sys.stderr, flush=True)
@@ -187,16 +192,23 @@ def main():
     elif w.int8k:
         k, ks = gqa.gqa_quantize_rows_int8(d["k"].to(dev))
         kw = dict(k_scale=ks)
+        if w.int8v:   # the producer's V codes, feature-major [4, 256, ld]
+            v, vs = gqa.gqa_quantize_v_int8(d["v"].to(dev))
+            kw["v_scale"] = vs
     else:
         k = d["k"].to(dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
     # KV-segment workspace (empty when the call runs unsplit), allocated before timing
-    ws_bytes = gqa.gqa_attn_prefill_workspace_size(w.q_len, w.kv_len, w.paged, w.int8k)
+    int8k_arg = 2 if w.int8v else int(w.int8k)
+    ws_bytes = gqa.gqa_attn_prefill_workspace_size(w.q_len, w.kv_len, w.paged, int8k_arg)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     def step():
-        gqa.gqa_attn_prefill_ws(q, k, v, out=out, workspace=ws, stream=stream, **kw)
+        if w.int8v:
+            gqa.gqa_attn_prefill_int8kv(q, k, kw["k_scale"], v, kw["v_scale"], out=out, stream=stream)
+        else:
+            gqa.gqa_attn_prefill_ws(q, k, v, out=out, workspace=ws, stream=stream, **kw)
 
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20)
@@ -238,10 +250,11 @@ def main():
     flops = 4.0 * HQ * D * w.pairs_per_head
     tflops = flops / (ms * 1e-3) / 1e12
     # algorithmic bytes: Q and out once, each K and V row once (int8 K: 1 byte a feature
-    # plus its scale), the block table
+    # plus its scale; int8 V: 1 byte a feature plus a scale per feature), the block table
     kv_rows = w.kv_len * HKV
     alg_bytes = (2 * w.q_len * HQ * D * 2 + kv_rows * D * (1 if w.int8k else 2)
-                 + kv_rows * D * 2 + (kv_rows * 4 if w.int8k else 0)
+                 + kv_rows * D * (1 if w.int8v else 2) + (kv_rows * 4 if w.int8k else 0)
+                 + (HKV * D * 4 if w.int8v else 0)
                  + (4 * ((w.kv_len + 15) // 16) if w.paged else 0))
     # the committed counter records are of the default build (query block 3)
     counters = load_counters(w.name) if args.query_block == 3 and args.library is None else None
@@ -256,7 +269,9 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
                     "frac": round(gbs / 8000.0, 4), "traffic": traffic, "hbm_gbs": hbm_gbs,
                     "mfma_busy": mfma_busy}
-    if w.int8k:
+    if w.int8v:
+        peak = PEAK_INT8_TOPS   # Q·K^T and P·V both on int8 MFMA
+    elif w.int8k:
         # Q·K^T on int8 MFMA, P·V on bf16 MFMA: time at peak is the sum of both halves
         t_peak = (flops / 2) / (PEAK_INT8_TOPS * 1e12) + (flops / 2) / (PEAK_BF16_TFLOPS * 1e12)
         peak = flops / t_peak / 1e12
@@ -277,13 +292,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8+bf16" if w.int8k else "bf16",
+        "dtype": "int8" if w.int8v else ("int8+bf16" if w.int8k else "bf16"),
         "data": "synthetic",
         "config": {"workload": w.name, "q_len": w.q_len, "kv_len": w.kv_len, "q_heads": HQ,
                    "kv_heads": HKV, "head_dim": D,
                    "kv_layout": ("paged16_splitd" if w.int8k else "paged16") if w.paged else "contiguous",
                    "keys": "int8" if w.int8k else "bf16",
-                   "variant": gqa.gqa_attn_prefill_plan(w.q_len, w.kv_len, w.paged, w.int8k)},
+                   "values": "int8" if w.int8v else "bf16",
+                   "variant": gqa.gqa_attn_prefill_plan(w.q_len, w.kv_len, w.paged, int8k_arg)},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -34,6 +34,8 @@ _STATUS_NAMES = {
 }
 # bytes of device scratch memory gqa_attn_prefill_noalloc holds per GPU
 NOALLOC_SCRATCH_BYTES = 64 << 20
+# longest history gqa_attn_prefill_int8kv accepts (its int32 sums stay below 2^31)
+INT8KV_MAX_KV = 1 << 17
 
 
 class GqaError(RuntimeError):
@@ -75,6 +77,10 @@ def library() -> ctypes.CDLL:
         lib.gqa_attn_prefill_workspace_size.argtypes = [i32, i32, ctypes.c_int, ctypes.c_int]
         lib.gqa_quantize_rows_int8.restype = ctypes.c_int
         lib.gqa_quantize_rows_int8.argtypes = [vp, i64, vp, vp, vp]
+        lib.gqa_attn_prefill_int8kv.restype = ctypes.c_int
+        lib.gqa_attn_prefill_int8kv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp]
+        lib.gqa_quantize_v_int8.restype = ctypes.c_int
+        lib.gqa_quantize_v_int8.argtypes = [vp, i32, i32, vp, vp, vp]
         lib.gqa_attn_prefill_plan.restype = ctypes.c_int
         lib.gqa_attn_prefill_plan.argtypes = [i32, i32, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_char_p, ctypes.c_size_t]
@@ -90,7 +96,8 @@ def gqa_status_string(status: int) -> str:
     return library().gqa_status_string(status).decode()
 
 
-def gqa_attn_prefill_plan(q_len: int, kv_len: int, paged: bool = False, int8k: bool = False) -> str:
+def gqa_attn_prefill_plan(q_len: int, kv_len: int, paged: bool = False, int8k: int = False) -> str:
+    """The launch a call would choose; int8k: 0 bf16 keys, 1 INT8 keys, 2 INT8 keys and values."""
     buf = ctypes.create_string_buffer(256)
     st = library().gqa_attn_prefill_plan(q_len, kv_len, int(paged), int(int8k), buf, 256)
     if st != GQA_OK:
@@ -299,3 +306,64 @@ def gqa_quantize_rows_int8(x: torch.Tensor, xq: torch.Tensor | None = None,
     if st != GQA_OK:
         raise GqaError(st, "gqa_quantize_rows_int8")
     return xq, scale
+
+
+def gqa_quantize_v_int8(v: torch.Tensor, v_ld: int | None = None, v_codes: torch.Tensor | None = None,
+                        v_scale: torch.Tensor | None = None, stream=None):
+    """INT8 codes of V per (KV head, feature) column for gqa_attn_prefill_int8kv (see
+    gqa_quantize_v_int8 in include/gqa_prefill.h). v: bf16 [kv_len, 4, 256]. Returns
+    (v_codes int8 [4, 256, v_ld], v_scale float32 [4, 256]); v_ld defaults to kv_len
+    rounded up to a multiple of 16."""
+    if v.device.type != "cuda":
+        raise ValueError("gqa_quantize_v_int8 runs on the GPU")
+    kv_len = v.shape[0]
+    _expect(v, "v", torch.bfloat16, (kv_len, NUM_KV_HEADS, HEAD_DIM), v.device)
+    v_ld = (kv_len + 15) // 16 * 16 if v_ld is None else v_ld
+    s = _launch_stream(v.device, stream)
+    if v_codes is None:
+        v_codes = _alloc_on(s, (NUM_KV_HEADS, HEAD_DIM, v_ld), torch.int8, v.device)
+    if v_scale is None:
+        v_scale = _alloc_on(s, (NUM_KV_HEADS, HEAD_DIM), torch.float32, v.device)
+    _expect(v_codes, "v_codes", torch.int8, (NUM_KV_HEADS, HEAD_DIM, v_ld), v.device)
+    _expect(v_scale, "v_scale", torch.float32, (NUM_KV_HEADS, HEAD_DIM), v.device)
+    st = library().gqa_quantize_v_int8(_ptr(v), kv_len, v_ld, _ptr(v_codes), _ptr(v_scale),
+                                       _stream_handle(s))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_quantize_v_int8")
+    return v_codes, v_scale
+
+
+def gqa_attn_prefill_int8kv(q: torch.Tensor, k: torch.Tensor, k_scale: torch.Tensor,
+                            v_codes: torch.Tensor, v_scale: torch.Tensor,
+                            q_scale: torch.Tensor | None = None, kv_len: int | None = None,
+                            out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Attention with INT8 keys, INT8 values and an INT8 P·V product (see
+    gqa_attn_prefill_int8kv in include/gqa_prefill.h). q: bf16 [q_len, 24, 256], or int8
+    codes with q_scale float32 [q_len, 24]; k int8 [kv_len, 4, 256] with k_scale float32
+    [kv_len, 4]; v_codes int8 [4, 256, v_ld] and v_scale float32 [4, 256] as
+    gqa_quantize_v_int8 returns them. Returns out (bf16 [q_len, 24, 256])."""
+    dev = q.device
+    s = _launch_stream(dev, stream)
+    q_len = q.shape[0]
+    kv_len = k.shape[0] if kv_len is None else kv_len
+    _expect(q, "q", torch.int8 if q_scale is not None else torch.bfloat16,
+            (q_len, NUM_Q_HEADS, HEAD_DIM), dev)
+    if q_scale is not None:
+        _expect(q_scale, "q_scale", torch.float32, (q_len, NUM_Q_HEADS), dev)
+    _expect(k, "k", torch.int8, (kv_len, NUM_KV_HEADS, HEAD_DIM), dev)
+    _expect(k_scale, "k_scale", torch.float32, (kv_len, NUM_KV_HEADS), dev)
+    if v_codes.dim() != 3:
+        raise ValueError("v_codes must be [4, 256, v_ld]")
+    v_ld = v_codes.shape[2]
+    _expect(v_codes, "v_codes", torch.int8, (NUM_KV_HEADS, HEAD_DIM, v_ld), dev)
+    _expect(v_scale, "v_scale", torch.float32, (NUM_KV_HEADS, HEAD_DIM), dev)
+    if out is None:
+        out = _alloc_on(s, (q_len, NUM_Q_HEADS, HEAD_DIM), torch.bfloat16, dev)
+    else:
+        _expect(out, "out", torch.bfloat16, (q_len, NUM_Q_HEADS, HEAD_DIM), dev)
+    st = library().gqa_attn_prefill_int8kv(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale),
+                                           _ptr(v_codes), _ptr(v_scale), v_ld, q_len, kv_len,
+                                           _ptr(out), _stream_handle(s))
+    if st != GQA_OK:
+        raise GqaError(st, "gqa_attn_prefill_int8kv")
+    return out

@@ -49,6 +49,13 @@
 //     v_mfma_i32_16x16x64_i8; the int32 score is scaled by sK·sQ·log2(e)/16 per
 //     score before the softmax ([INT8 QK §1]), for the next tile during the P·V
 //     steps of the current one.
+//   * with INT8 values as well ([INT8 QK §6] names INT8 PV and defines nothing more; the
+//     reading taken: V codes per (KV head, feature) over the sequence, stored feature-major
+//     by the producer, and P codes round(127 * 2^(y - max)) against each column's exact
+//     maximum), a first sweep over the history finds those maxima, then one pass forms the
+//     P codes in place of bf16 P and runs P·V on v_mfma_i32_16x16x64_i8 into int32
+//     accumulators; the V^T tile is laid out so that each lane's 16 keys of a feature are
+//     one ds_read_b128.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -100,6 +107,8 @@ constexpr int kSplitBelow = 256;
 // which compares greater too.
 constexpr float kOverSum = 4294967296.0f;
 constexpr float kLog2eOver16 = 1.4426950408889634f / 16.0f;
+// INT8 values: P codes are 127 * 2^(y - max), the exponent shifted by log2(127)
+constexpr float kLog2Of127 = 6.988684686772166f;
 
 // key scales of a tile: a 256-byte area per wave, [KV head][16 key slots] (a 32-key tile
 // uses 8 of the 16 slots of each wave)
@@ -119,7 +128,7 @@ struct Params {
   const uint8_t* q;        // bf16 [q_len, 24, 256], or int8 codes of Q when qsc is set
   const float* qsc;        // INT8 keys, Q quantised beforehand: sQ [q_len, 24]; else null
   const uint8_t* k;        // bf16 or int8, contiguous or paged
-  const uint8_t* v;        // bf16, contiguous or paged
+  const uint8_t* v;        // bf16, contiguous or paged; INT8 values: codes [4, 256, v_ld]
   const int32_t* bt;       // block table or null
   const float* ks;         // key scales [kv_len, 4] or null
   uint8_t* out;            // bf16 [q_len, 24, 256]
@@ -131,6 +140,8 @@ struct Params {
   int32_t n_plain;         // n_seg > 1: the shortest token blocks 0 .. n_plain - 1 run whole
   float* ws_o;             // n_seg > 1: unnormalised O [n_seg, split rows, 24, 256]
   float* ws_ml;            // n_seg > 1: (reference maximum, row sum) [n_seg, split rows, 24, 2]
+  const float* vs;         // INT8 values: sV [4, 256]; else null
+  int32_t v_ld;            // INT8 values: tokens per stored feature row of V
 };
 
 // Workgroup shape for QB 16-column query blocks per wave. QB = 3 and QB = 2 map a
@@ -372,9 +383,60 @@ struct ScaleCopy {
   }
 };
 
+// INT8 values: the producer stores the codes feature-major, [4, 256, ld] with the token
+// index fastest, so a tile (64 keys of all 256 features of KV head g) is one 64-byte run
+// per feature. In LDS each feature f is a 64-byte row; its 16-byte slot s holds, as dwords
+// kb = 0..3, the keys 16 kb + 4 L .. 16 kb + 4 L + 3 with L = s ^ ((f >> 2) & 3). Lane
+// (L, c) of the P·V step needs for feature c of a 16-feature block exactly the 16 keys whose
+// scores its S^T registers hold (keys 16 kb + 4 L + r, r = 0..3), in that order: one
+// ds_read_b128 of slot L ^ ((c >> 2) & 3), and the XOR puts the 16 lanes of a lane group
+// in 16 different 16-byte bank groups. A copy instruction fills 4 feature rows (256 B, lane
+// l writing dword l), one dword (4 keys) per lane; wave w copies features 64 w .. 64 w + 63
+// in 16 instructions. Feature 64 w + 4 I + (l >> 4) of instruction I has swizzle I & 3, so
+// a lane needs 4 source offsets. The descriptor covers the wave's 64 rows up to the tile's
+// last key, cut at the end of the array; a tile at or past kv_len has no range at all.
+struct VtCopy {
+  static constexpr int kInsts = 16;
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t lds;   // LDS address of the wave's first feature row in the destination tile
+  uint32_t ld;    // bytes between feature rows
+
+  // source offset of lane l for the instructions I with I % 4 == J
+  static __device__ __forceinline__ uint32_t lane_offset(int lane, int J, int ld) {
+    const int d = lane & 15;   // destination dword in the feature row: slot d >> 2, key block d & 3
+    return (uint32_t)((lane >> 4) * ld + 16 * (d & 3) + 4 * ((d >> 2) ^ J));
+  }
+  __device__ __forceinline__ VtCopy(const Params& p, int g, int kbase, int w, uint32_t lds_tile) {
+    const int n = min(max(p.kv_len - kbase, 0), kKt);
+    const int64_t row0 = (int64_t)g * kD + 64 * w;
+    const int64_t first = row0 * p.v_ld + kbase;
+    const int64_t left = (int64_t)kHkv * kD * p.v_ld - first;   // bytes from the first to the end
+    const int64_t span = (int64_t)63 * p.v_ld + kKt;
+    const int bytes = n > 0 ? (int)min(span, left) : 0;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.v + first), (short)0,
+                                             __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+    lds = lds_tile + 64 * w * kKt;
+    ld = (uint32_t)p.v_ld;
+  }
+  // the whole offset goes into the lane's offset, which the range check covers
+  template <int I>
+  __device__ __forceinline__ void issue(const uint32_t (&vto)[4]) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds + I * 256), 4, vto[I & 3] + (4 * I) * ld,
+                                             0, 0, 0);
+  }
+};
+
 __device__ __forceinline__ void wait_vm_all() {
   // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
   __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// s_waitcnt vmcnt(N): a wave's vector memory operations complete in order, so at most N
+// outstanding means all but its N most recent are done
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
 // ---- explicit LDS reads ----
@@ -544,8 +606,8 @@ __device__ __forceinline__ void mfma_pv(f32x4& acc, const bf16x8& v, const bf16x
 // NOPS wait states. Before the accumulators are zeroed or read by the vector ALU after
 // MFMAs, 24 wait states cover the longest MFMA-write to vector-access distance of the
 // 16x16x32 MFMAs; after zeroing, 2 cover the vector-write to MFMA-read distance.
-template <int NOPS, int QB>
-__device__ __forceinline__ void agpr_fence(f32x4 (&o)[16][QB]) {
+template <int NOPS, int QB, class T>
+__device__ __forceinline__ void agpr_fence(T (&o)[16][QB]) {
   static_assert(NOPS == 2 || NOPS == 24, "wait states");
   if constexpr (NOPS == 2)
     asm volatile("s_nop 1" : "+a"(o[0][0]));
@@ -589,16 +651,73 @@ struct PvStep {
   }
 };
 
+// ---- INT8 values: O^T += Vq^T · Pq^T in int32 ----
+// The V^T operand of 16 features x 64 keys is one ds_read_b128 per lane (see VtCopy), so a
+// step is one read and QB MFMAs of v_mfma_i32_16x16x64_i8 over the whole 64-key tile; the
+// same hazards as mfma_pv apply (FIRST: P was written by the vector ALU).
+template <bool FIRST>
+__device__ __forceinline__ void mfma_pv_i8(i32x4& acc, const i32x4& v, const i32x4& p) {
+  if constexpr (FIRST)
+    asm("s_nop 1\n\tv_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
+  else
+    asm("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
+}
+
+template <int N>
+__device__ __forceinline__ void vt8_wait(u32x4& f) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(f) : "i"(N));
+}
+
+// Step N = feature block db (16 features) of the 16 steps of a tile; V^T fragment db at
+// vbase + db * 1024 (16 rows of 64 B). Fragments travel in a ring of kVtDepth + 1 reads.
+template <int N, int QB>
+struct PvStepI8 {
+  static constexpr int kSteps = kD / 16;
+  template <class Extra>
+  static __device__ __forceinline__ void run(u32x4 (&vf)[kVtDepth + 1], uint32_t vbase,
+                                             const i32x4 (&pq)[QB], const i32x4& ones,
+                                             i32x4 (&o)[16][QB], i32x4 (&lacc)[QB], Extra&& extra) {
+    extra(std::integral_constant<int, N>{});
+    constexpr int kAhead = (kSteps - 1 - N) < kVtDepth ? (kSteps - 1 - N) : kVtDepth;
+    if constexpr (N + kVtDepth < kSteps)
+      vf[(N + kVtDepth) % (kVtDepth + 1)] = lds_read_b128<(N + kVtDepth) * 1024>(vbase);
+    vt8_wait<kAhead>(vf[N % (kVtDepth + 1)]);
+    const i32x4 v = __builtin_bit_cast(i32x4, vf[N % (kVtDepth + 1)]);
+#pragma unroll
+    for (int b = 0; b < QB; ++b) mfma_pv_i8<N == 0>(o[N][b], v, pq[b]);
+    if constexpr (N == 0) {
+      // row sums from the same codes
+#pragma unroll
+      for (int b = 0; b < QB; ++b) lacc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, pq[b], lacc[b], 0, 0, 0);
+    }
+    if constexpr (N + 1 < kSteps) PvStepI8<N + 1, QB>::run(vf, vbase, pq, ones, o, lacc, extra);
+  }
+};
+
 template <bool PAGED, bool INT8K, int QB>
 constexpr int k_tile_bytes() {
   return (INT8K ? 2 : 4) * kSegStride;
 }
 
-// LDS: two K tiles, two V tiles, (INT8 keys) a 3-slot ring of key-scale rows, and
-// two slots of one restart flag per wave.
-template <bool PAGED, bool INT8K, int QB>
+// bytes of a V tile: 64 keys x 256 features of bf16, or of INT8 codes
+template <bool INT8V>
+constexpr int v_tile_bytes() {
+  return (INT8V ? 2 : 4) * kSegStride;
+}
+
+// key-scale slots: a ring of 3 in the main loop; INT8 values add a fourth for the
+// maximum sweep, which keeps three tiles in flight
+template <bool INT8K, bool INT8V>
+constexpr int sk_slots() {
+  return INT8V ? 4 : (INT8K ? 3 : 0);
+}
+
+// LDS: two K tiles, two V tiles, (INT8 keys) the ring of key-scale rows, and two slots of
+// one restart flag per wave.
+template <bool PAGED, bool INT8K, int QB, bool INT8V = false>
 constexpr int lds_bytes() {
-  return 2 * k_tile_bytes<PAGED, INT8K, QB>() + 2 * 4 * kSegStride + (INT8K ? 3 * kSkTile : 0) + 32;
+  return 2 * k_tile_bytes<PAGED, INT8K, QB>() + 2 * v_tile_bytes<INT8V>() +
+         sk_slots<INT8K, INT8V>() * kSkTile + 32;
 }
 
 // The whole workgroup program. SPLIT selects the P·V form (see the file header); it
@@ -607,16 +726,19 @@ constexpr int lds_bytes() {
 // Software pipeline over KV tiles: iteration j holds S(j) from the previous
 // iteration, computes P(j) while the MFMAs of S(j+1) = K(j+1)·Q^T run, then
 // O += V(j)·P(j). LDS holds K(j+1) and V(j) while K(j+2) and V(j+1) are copied in.
-template <bool PAGED, bool INT8K, int QB, bool SPLIT>
+template <bool PAGED, bool INT8K, int QB, bool SPLIT, bool INT8V = false>
 __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
+  static_assert(!INT8V || (INT8K && !PAGED && !SPLIT && QB > 1 && kKt == 64),
+                "INT8 values: contiguous INT8 keys, prefill shapes, 64-key tiles");
   using S = Shape<QB>;
   constexpr bool kPM = PAGED && INT8K;   // page-major K tiles (the split-d cache)
   using Q = QK<INT8K, QB, kPM>;
   using Acc = typename Q::Acc;
   constexpr int kKTile = k_tile_bytes<PAGED, INT8K, QB>();
+  constexpr int kVTile = v_tile_bytes<INT8V>();
   constexpr int kVOff = 2 * kKTile;                    // V tiles follow the two K tiles
-  constexpr int kSkOff = kVOff + 8 * kSegStride;       // then the key-scale ring
-  constexpr int kFlagOff = kSkOff + (INT8K ? 3 * kSkTile : 0);   // then the restart flags
+  constexpr int kSkOff = kVOff + 2 * kVTile;           // then the key-scale ring
+  constexpr int kFlagOff = kSkOff + sk_slots<INT8K, INT8V>() * kSkTile;   // then the restart flags
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -669,11 +791,18 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   // ---- tile copies (this wave's 16 keys of each tile) ----
   using KCopy = WaveCopy<PAGED, INT8K ? kD : 2 * kD, false, PAGED && INT8K>;
   using SCopy = ScaleCopy<PAGED>;
-  using VCopy = WaveCopy<PAGED, 2 * kD, true>;
+  using VCopy = typename std::conditional<INT8V, VtCopy, WaveCopy<PAGED, 2 * kD, true>>::type;
   const uint32_t smem_addr = lds_addr(smem);
   const uint32_t sk_addr = smem_addr + kSkOff;   // key-scale ring (INT8 keys)
   const uint32_t kvo[2] = {KCopy::lane_offset(lane, 0), KCopy::lane_offset(lane, kHalves - 1)};
-  const uint32_t vvo[2] = {VCopy::lane_offset(lane, 0), VCopy::lane_offset(lane, kHalves - 1)};
+  uint32_t vvo[INT8V ? 4 : 2];
+  if constexpr (INT8V) {
+#pragma unroll
+    for (int J = 0; J < 4; ++J) vvo[J] = VtCopy::lane_offset(lane, J, p.v_ld);
+  } else {
+    vvo[0] = VCopy::lane_offset(lane, 0);
+    vvo[1] = VCopy::lane_offset(lane, kHalves - 1);
+  }
   const uint32_t svo = SCopy::lane_offset(lane);
   const int skey = lane & 15;   // the key whose scales this lane copies
   // Paged: the physical block of this wave's 16 keys of the tile at kbase (an entry
@@ -695,8 +824,13 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
                  smem_addr + buf * kKTile + (kPM ? w * kPageBytes : kWaveKeys * w * 128));
   };
   auto vcopy = [&](int kbase, int buf, int blk) {
-    return VCopy(p, p.v, g, kbase + kWaveKeys * w, blk,
-                 smem_addr + kVOff + buf * 4 * kSegStride + kWaveKeys * w * 128);
+    if constexpr (INT8V) {
+      (void)blk;
+      return VCopy(p, g, kbase, w, smem_addr + kVOff + buf * kVTile);
+    } else {
+      return VCopy(p, p.v, g, kbase + kWaveKeys * w, blk,
+                   smem_addr + kVOff + buf * kVTile + kWaveKeys * w * 128);
+    }
   };
   auto scopy = [&](int kbase, int slot, int blk) {
     return SCopy(p, kbase + kWaveKeys * w, blk, sk_addr + slot * kSkTile + w * 256);
@@ -713,10 +847,20 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     static_for<0, VCopy::kInsts>([&](auto ic) { vc.template issue<decltype(ic)::value>(vvo); });
   };
 
-  // start the first copies before the Q prologue
-  copy_k_all(j0 * kKt, j0 & 1, j0 % 3);
-  copy_v_all(j0 * kKt, j0 & 1);
-  if (j1 - j0 > 1) copy_k_all((j0 + 1) * kKt, (j0 + 1) & 1, (j0 + 1) % 3);
+  // INT8 values: the maximum sweep below runs first, over every tile of the history, with
+  // three tiles of K in flight in the four K and V buffers and the four key-scale slots
+  constexpr int kSweepDepth = 3;
+  constexpr int kSweepPerTile = KCopy::kInsts + 1;   // this wave's copies per sweep tile
+  static_assert(!INT8V || 2 * kSweepPerTile < 16, "sweep copies in flight");
+  if constexpr (INT8V) {
+    static_assert(kVTile == kKTile, "the sweep uses the V buffers as K buffers");
+    for (int t = 0; t < min(kSweepDepth, ntiles); ++t) copy_k_all(t * kKt, t & 3, t & 3);
+  } else {
+    // start the first copies before the Q prologue
+    copy_k_all(j0 * kKt, j0 & 1, j0 % 3);
+    copy_v_all(j0 * kKt, j0 & 1);
+    if (j1 - j0 > 1) copy_k_all((j0 + 1) * kKt, (j0 + 1) & 1, (j0 + 1) % 3);
+  }
 
   // ---- prologue: Q fragments (B operand of S^T = K·Q^T) ----
   typename Q::Frag qf[QB][Q::kSteps];
@@ -798,10 +942,15 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  // INT8 values: lane (L, c) reads slot L ^ ((c >> 2) & 3) of feature row c of each
+  // 16-feature block (VtCopy)
+  const uint32_t vt8_off = c * kKt + 16 * (L ^ ((c >> 2) & 3));
+  const i32x4 ones8 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 
   // ---- accumulators: O^T blocks [feature block db][query block b], row sums ----
-  f32x4 o[16][QB];
-  f32x4 lacc[QB];
+  using OAcc = typename std::conditional<INT8V, i32x4, f32x4>::type;   // int32 with INT8 values
+  OAcc o[16][QB];
+  OAcc lacc[QB];
   float m[QB];   // reference maximum per column (log2 units), fixed during a pass
   Acc sacc[QB][kKb];
   int* const flags = reinterpret_cast<int*>(smem + kFlagOff);
@@ -965,8 +1114,8 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
 #pragma unroll
-      for (int db = 0; db < 16; ++db) o[db][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-      lacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int db = 0; db < 16; ++db) o[db][b] = OAcc{0, 0, 0, 0};
+      lacc[b] = OAcc{0, 0, 0, 0};
     }
     agpr_fence<2>(o);
     if (pass == 0 && tid < 8) flags[tid] = 0;
@@ -996,7 +1145,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     auto body = [&](int j, auto mask_c) -> bool {
       const int kbase = j * kKt;
       const uint8_t* knext = smem + ((j + 1) & 1) * kKTile;             // K(j+1) (stale on the last tile)
-      const uint8_t* vcur = smem + kVOff + (j & 1) * 4 * kSegStride;   // V(j)
+      const uint8_t* vcur = smem + kVOff + (j & 1) * kVTile;   // V(j)
       // copies of K(j+2) and V(j+1), spread evenly over the K steps of both halves (one
       // per step for bf16 keys): the vector memory path moves about 64 B per clock per CU,
       // so the 64 KiB of a tile need a good part of the iteration, and issuing them in a
@@ -1035,6 +1184,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       // time: the half of S(j) being turned into P is copied out of the accumulators
       // before the MFMAs of S(j+1) overwrite them ----
       bf16x8 ph[QB][2], pl[QB][2];
+      uint32_t pq8[QB][4];   // INT8 values: P codes, dword kb = keys 16 kb + 4 L .. + 3
       const uint32_t kn = lds_addr(knext);
       auto half = [&](auto hc) {
         constexpr int H = decltype(hc)::value;
@@ -1049,14 +1199,27 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
 #pragma unroll
           for (int b = 0; b < QB; ++b) {
             if (st == ((b + 1) * Q::kSteps) / QB - 1) {
-              const float nm = -m[b];
-              f32x8 pv;
+              if constexpr (INT8V) {
+                // Pq = round(127 * 2^(y - max)): the exponent already holds + log2(127); the
+                // clamp keeps a code that rounding lifts past 127 at 127
+                uint32_t wv[2] = {0u, 0u};
 #pragma unroll
-              for (int e = 0; e < 8; ++e)
-                pv[e] = __builtin_amdgcn_exp2f(INT8K ? sc[b][e] : __builtin_fmaf(sc[b][e], scale[b], nm));
-              ph[b][H] = __builtin_convertvector(pv, bf16x8);
-              if constexpr (SPLIT)
-                pl[b][H] = __builtin_convertvector(pv - __builtin_convertvector(ph[b][H], f32x8), bf16x8);
+                for (int e = 0; e < 8; ++e) {
+                  const float x = fminf(__builtin_amdgcn_exp2f(sc[b][e]), 127.0f);
+                  wv[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(x), e & 3, wv[e >> 2]);
+                }
+                pq8[b][2 * H] = wv[0];
+                pq8[b][2 * H + 1] = wv[1];
+              } else {
+                const float nm = -m[b];
+                f32x8 pv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                  pv[e] = __builtin_amdgcn_exp2f(INT8K ? sc[b][e] : __builtin_fmaf(sc[b][e], scale[b], nm));
+                ph[b][H] = __builtin_convertvector(pv, bf16x8);
+                if constexpr (SPLIT)
+                  pl[b][H] = __builtin_convertvector(pv - __builtin_convertvector(ph[b][H], f32x8), bf16x8);
+              }
             }
           }
         };
@@ -1068,7 +1231,31 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       // ---- O^T += V^T(j) · P^T(j); INT8 keys: S(j+1) is scaled between the steps, where
       // the vector ALU has room (the Q·K^T halves above are short on it: half as many
       // MFMAs as with bf16 keys for the same softmax work) ----
-      {
+      if constexpr (INT8V) {
+        u32x4 sr[4];   // scales of tile j + 1 (copied two iterations ago)
+        sk_read(sk_addr + ((j + 1) % 3) * kSkTile, sr);
+        const uint32_t vb = lds_addr(vcur) + vt8_off;
+        u32x4 vf[kVtDepth + 1];
+        static_for<0, kVtDepth>([&](auto nc) {   // the first kVtDepth steps' reads
+          constexpr int N = decltype(nc)::value;
+          vf[N] = lds_read_b128<N * 1024>(vb);
+        });
+        i32x4 pqv[QB];
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+          pqv[b] = i32x4{(int)pq8[b][0], (int)pq8[b][1], (int)pq8[b][2], (int)pq8[b][3]};
+        PvStepI8<0, QB>::run(vf, vb, pqv, ones8, o, lacc, [&](auto nc) {
+          constexpr int N = decltype(nc)::value;
+          // at step 1 only the kVtDepth reads of steps 1 .. kVtDepth are younger than the
+          // scale reads: the wait costs nothing and marks them valid
+          if constexpr (N == 1) lds_wait4<kVtDepth>(sr[0], sr[1], sr[2], sr[3]);
+          if constexpr (N >= 2 && N - 2 < kKb * QB) {
+            constexpr int u = N - 2;
+            scale_unit(std::integral_constant<int, u / QB>{}, std::integral_constant<int, u % QB>{}, sr,
+                       std::true_type{});
+          }
+        });
+      } else {
         u32x4 sr[4];   // scales of tile j + 1 (copied two iterations ago)
         if constexpr (INT8K) sk_read(sk_addr + ((j + 1) % 3) * kSkTile, sr);
         uint32_t vbase[4];
@@ -1124,7 +1311,42 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     return restart;
   };
 
-  if (main_pass(std::integral_constant<int, 0>{})) {
+  if constexpr (INT8V) {
+    // ---- exact column maxima over every visible key of the whole history, then the one
+    // pass, with the maxima as reference (no restart: every exponent is at most log2 127) ----
+    const int n_unmasked = (off + t0 + 1) / kKt;   // tiles before the first query's diagonal
+    float lm[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) lm[b] = -__builtin_inff();
+    for (int t = 0; t < ntiles; ++t) {
+      const int ahead = min(ntiles - 1 - t, kSweepDepth - 1);   // tiles copied after t so far
+      if (ahead >= 2)
+        wait_vm<2 * kSweepPerTile>();
+      else if (ahead == 1)
+        wait_vm<kSweepPerTile>();
+      else
+        wait_vm<0>();
+      __syncthreads();   // tile t landed for every wave; every wave is done with tile t - 1
+      if (t + kSweepDepth < ntiles)
+        copy_k_all((t + kSweepDepth) * kKt, (t + kSweepDepth) & 3, (t + kSweepDepth) & 3);
+      qk_tile(smem_addr + (t & 3) * kKTile);
+      scale_tile(sk_addr + (t & 3) * kSkTile);
+      float sc0[QB][8], sc1[QB][8], scale[QB];
+      if (t < n_unmasked) {
+        half_scores(std::false_type{}, t * kKt, 0, sc0, scale);
+        half_scores(std::false_type{}, t * kKt, 1, sc1, scale);
+      } else {
+        half_scores(std::true_type{}, t * kKt, 0, sc0, scale);
+        half_scores(std::true_type{}, t * kKt, 1, sc1, scale);
+      }
+#pragma unroll
+      for (int b = 0; b < QB; ++b) lm[b] = fmaxf(lm[b], fmaxf(lane_max(sc0, b), lane_max(sc1, b)));
+    }
+#pragma unroll
+    for (int b = 0; b < QB; ++b) m[b] = xor32_max(xor16_max(lm[b])) - kLog2Of127;
+    __syncthreads();   // every wave is done with the sweep's buffers
+    main_pass(std::integral_constant<int, 1>{});
+  } else if (main_pass(std::integral_constant<int, 0>{})) {
     // ---- exact column maxima over every visible key (max-only sweep), then pass 1 ----
 #pragma unroll
     for (int b = 0; b < QB; ++b) m[b] = -__builtin_inff();
@@ -1144,46 +1366,71 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   }
 
   agpr_fence<24>(o);
-  if (unit.nseg > 1) {
-    // ---- epilogue of one KV segment: unnormalised O, the reference maximum (log2
-    // units, scale included) and the row sum, merged by merge_segments_kernel ----
+  if constexpr (INT8V) {
+    // ---- epilogue: O = sV * (Vq^T Pq^T) / l -> bf16 ----
+    float inv[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) inv[b] = 1.0f / (float)lacc[b][0];
     if (tok_ok) {
-      const size_t row0 = (seg * ws_rows + (tok - q0)) * kHq + head0;
-#pragma unroll
-      for (int b = 0; b < QB; ++b) {
-        float* orow = p.ws_o + (row0 + b) * kD;
-#pragma unroll
-        for (int db = 0; db < 16; ++db) *reinterpret_cast<f32x4*>(orow + 16 * db + 4 * L) = o[db][b];
-        if (L == 0) *reinterpret_cast<float2*>(p.ws_ml + (row0 + b) * 2) = make_float2(m[b], lacc[b][0]);
-      }
-    }
-    return;
-  }
-  // ---- epilogue: O / l -> bf16 ----
-#pragma unroll
-  for (int b = 0; b < QB; ++b) {
-    const float inv = 1.0f / lacc[b][0];
-    if (tok_ok) {
-      uint8_t* orow = p.out + ((size_t)tok * kHq + head0 + b) * kD * 2;
 #pragma unroll
       for (int db = 0; db < 16; ++db) {
-        const f32x4 y = o[db][b] * inv;
-        const bf16x4 yb = __builtin_convertvector(y, bf16x4);
-        *reinterpret_cast<bf16x4*>(orow + (16 * db + 4 * L) * 2) = yb;
+        const f32x4 sv = *reinterpret_cast<const f32x4*>(p.vs + g * kD + 16 * db + 4 * L);
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+          f32x4 y;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[r] = (float)o[db][b][r] * sv[r] * inv[b];
+          uint8_t* orow = p.out + ((size_t)tok * kHq + head0 + b) * kD * 2;
+          *reinterpret_cast<bf16x4*>(orow + (16 * db + 4 * L) * 2) = __builtin_convertvector(y, bf16x4);
+        }
+      }
+    }
+  } else {
+    if (unit.nseg > 1) {
+      // ---- epilogue of one KV segment: unnormalised O, the reference maximum (log2
+      // units, scale included) and the row sum, merged by merge_segments_kernel ----
+      if (tok_ok) {
+        const size_t row0 = (seg * ws_rows + (tok - q0)) * kHq + head0;
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+          float* orow = p.ws_o + (row0 + b) * kD;
+#pragma unroll
+          for (int db = 0; db < 16; ++db) *reinterpret_cast<f32x4*>(orow + 16 * db + 4 * L) = o[db][b];
+          if (L == 0) *reinterpret_cast<float2*>(p.ws_ml + (row0 + b) * 2) = make_float2(m[b], lacc[b][0]);
+        }
+      }
+      return;
+    }
+    // ---- epilogue: O / l -> bf16 ----
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const float inv = 1.0f / lacc[b][0];
+      if (tok_ok) {
+        uint8_t* orow = p.out + ((size_t)tok * kHq + head0 + b) * kD * 2;
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+          const f32x4 y = o[db][b] * inv;
+          const bf16x4 yb = __builtin_convertvector(y, bf16x4);
+          *reinterpret_cast<bf16x4*>(orow + (16 * db + 4 * L) * 2) = yb;
+        }
       }
     }
   }
 }
 
-template <bool PAGED, bool INT8K, int QB>
+template <bool PAGED, bool INT8K, int QB, bool INT8V = false>
 __global__ __launch_bounds__(kThreads, 1) void gqa_prefill_kernel(const Params p) {
   using S = Shape<QB>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[lds_bytes<PAGED, INT8K, QB>()];
-  const int t0 = unit_of<QB>(p, blockIdx.x).tblk * S::kTokPerWg;
-  if (p.kv_len - p.q_len + t0 + 1 < kSplitBelow)
-    run<PAGED, INT8K, QB, true>(p, smem);
-  else
-    run<PAGED, INT8K, QB, false>(p, smem);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[lds_bytes<PAGED, INT8K, QB, INT8V>()];
+  if constexpr (INT8V) {
+    run<false, true, QB, false, true>(p, smem);   // P codes carry no low part
+  } else {
+    const int t0 = unit_of<QB>(p, blockIdx.x).tblk * S::kTokPerWg;
+    if (p.kv_len - p.q_len + t0 + 1 < kSplitBelow)
+      run<PAGED, INT8K, QB, true>(p, smem);
+    else
+      run<PAGED, INT8K, QB, false>(p, smem);
+  }
 }
 
 // ---- merge of KV segments ----
@@ -1292,6 +1539,48 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint8_t* x, in
   if (lane == 0) scale[row] = s;
 }
 
+// ---- standalone V quantiser for INT8 values: codes per (KV head, feature) column ----
+// The per-row rule of the Q/K quantiser (float32 max|x| / 127 by IEEE division,
+// round-half-even of x / s, clamp to [-127, 127], a zero column gives s = 0) applied to
+// each column of V along the tokens. A workgroup per (KV head, 64-feature block): the
+// column maxima over all tokens (wave w takes every 4th token, a lane one feature), then
+// the codes, written feature-major [4, 256, ld] through an LDS tile of 64 tokens x 64
+// features so that each feature row is written 16 bytes at a time; positions kv_len ..
+// ld - 1 get code 0. A producer-side step, outside the attention call.
+__global__ __launch_bounds__(256) void quantize_v_kernel(const uint8_t* v, int32_t kv_len, int32_t ld,
+                                                         int8_t* vq, float* vs) {
+  const int g = blockIdx.x >> 2, fb = blockIdx.x & 3;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int f = 64 * fb + lane;
+  const __bf16* vb = reinterpret_cast<const __bf16*>(v);
+  __shared__ float part[4][64];
+  __shared__ __attribute__((aligned(16))) int8_t tile[64][80];
+  float amax = 0.0f;
+  for (int t = w; t < kv_len; t += 4) amax = fmaxf(amax, fabsf((float)vb[((size_t)t * kHkv + g) * kD + f]));
+  part[w][lane] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(part[0][lane], part[1][lane]), fmaxf(part[2][lane], part[3][lane]));
+  const float s = amax / 127.0f;
+  if (w == 0) vs[g * kD + f] = s;
+  const int r = threadIdx.x >> 2, qd = threadIdx.x & 3;   // writer: feature row r, 16-token chunk qd
+  for (int t0 = 0; t0 < ld; t0 += 64) {
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int t = t0 + 16 * w + i;
+      const float x = t < kv_len ? (float)vb[((size_t)t * kHkv + g) * kD + f] : 0.0f;
+      float c = (s == 0.0f) ? 0.0f : __builtin_rintf(x / s);
+      c = fminf(fmaxf(c, -127.0f), 127.0f);
+      tile[lane][16 * w + i] = (int8_t)(int)c;
+    }
+    __syncthreads();
+    const int t = t0 + 16 * qd;
+    if (t < ld)
+      *reinterpret_cast<uint4*>(vq + ((size_t)g * kD + 64 * fb + r) * ld + t) =
+          *reinterpret_cast<const uint4*>(&tile[r][16 * qd]);
+    __syncthreads();
+  }
+}
+
 // ---- host side ----
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -1315,7 +1604,7 @@ struct Launch {
 constexpr int kDefaultQB = GQA_DEFAULT_QB;
 
 template <int QB>
-Launch shape_launch(int32_t q_len, bool int8k) {
+Launch shape_launch(int32_t q_len, bool int8k, bool int8v = false) {
   using S = Shape<QB>;
   const int n_tblk = (q_len + S::kTokPerWg - 1) / S::kTokPerWg;
   Launch lc;
@@ -1325,7 +1614,8 @@ Launch shape_launch(int32_t q_len, bool int8k) {
   lc.per_tblk = S::kSplitsPerGroup;
   lc.workgroups = n_tblk * kHkv * S::kSplitsPerGroup;
   lc.threads = kThreads;
-  lc.lds_bytes = int8k ? lds_bytes<false, true, QB>() : lds_bytes<false, false, QB>();
+  lc.lds_bytes = int8v ? lds_bytes<false, true, QB, true>()
+                      : (int8k ? lds_bytes<false, true, QB>() : lds_bytes<false, false, QB>());
   return lc;
 }
 
@@ -1516,6 +1806,21 @@ Launch plan_for(int32_t q_len, int32_t kv_len, bool paged, bool int8k) {
   return lc;
 }
 
+// INT8 values: contiguous INT8 keys, the prefill shape at every q_len (no decode shape),
+// the whole history in one piece
+Launch plan_int8kv(int32_t q_len) {
+  Launch lc = shape_launch<kDefaultQB>(q_len, true, true);
+  lc.name = lc.qb == 3 ? "int8kv_contiguous_t32h6" GQA_KT_NAME(GQA_KT) : "int8kv_contiguous_t64h2" GQA_KT_NAME(GQA_KT);
+  return lc;
+}
+
+int check_int8kv_lengths(int32_t q_len, int32_t kv_len) {
+  const int st = check_prefill_lengths(q_len, kv_len);
+  if (st != GQA_OK) return st;
+  if (kKt != 64 || kv_len > GQA_INT8KV_MAX_KV) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
 int scratch_on(hipStream_t stream, void** ptr);
 
 // Shared by the entry points; `allow_split` is false for the call without a workspace,
@@ -1662,6 +1967,19 @@ int gqa_attn_prefill_plan(int32_t q_len, int32_t kv_len, int paged, int int8k, c
     snprintf(buf, n, "error: %s", gqa_status_string(st));
     return st;
   }
+  if (int8k == 2) {   // INT8 values: contiguous only, one piece
+    st = paged ? GQA_ERR_UNSUPPORTED : check_int8kv_lengths(q_len, kv_len);
+    if (st != GQA_OK) {
+      snprintf(buf, n, "error: %s", gqa_status_string(st));
+      return st;
+    }
+    const Launch lc = plan_int8kv(q_len);
+    snprintf(buf, n,
+             "variant=%s workgroups=%d threads=%d lds_bytes=%d segments=1 whole_token_blocks=%d "
+             "workspace_bytes=0",
+             lc.name, lc.workgroups, lc.threads, lc.lds_bytes, lc.n_tblk);
+    return GQA_OK;
+  }
   const Launch lc = plan_for(q_len, kv_len, paged != 0, int8k != 0);
   const SegPlan sp = segments_for(q_len, kv_len, lc);
   snprintf(buf, n,
@@ -1673,7 +1991,7 @@ int gqa_attn_prefill_plan(int32_t q_len, int32_t kv_len, int paged, int int8k, c
 }
 
 size_t gqa_attn_prefill_workspace_size(int32_t q_len, int32_t kv_len, int paged, int int8k) {
-  if (check_prefill_lengths(q_len, kv_len) != GQA_OK) return 0;
+  if (check_prefill_lengths(q_len, kv_len) != GQA_OK || int8k == 2) return 0;
   const Launch lc = plan_for(q_len, kv_len, paged != 0, int8k != 0);
   return workspace_bytes_for(q_len, lc, segments_for(q_len, kv_len, lc));
 }
@@ -1708,6 +2026,56 @@ int gqa_attn_prefill_qint8(const void* q_codes, const float* q_scale, const void
   if (q_scale == nullptr || k_scale == nullptr) return GQA_ERR_NULL_ARG;
   return prefill(q_codes, q_scale, k, v, block_table, num_blocks, k_scale, q_len, kv_len, out,
                  workspace, workspace_bytes, true, stream);
+}
+
+int gqa_attn_prefill_int8kv(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                            const void* v_codes, const float* v_scale, int32_t v_ld, int32_t q_len,
+                            int32_t kv_len, void* out, void* stream) {
+  int st = check_prefill_lengths(q_len, kv_len);
+  if (st != GQA_OK) return st;
+  if (q_len == 0) return GQA_OK;
+  if (v_ld < kv_len || v_ld > GQA_MAX_LEN || (v_ld & 15) != 0) return GQA_ERR_BAD_LENGTH;
+  if (q == nullptr || k == nullptr || k_scale == nullptr || v_codes == nullptr || v_scale == nullptr ||
+      out == nullptr)
+    return GQA_ERR_NULL_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v_codes, 16) || !aligned(out, 16) ||
+      !aligned(k_scale, 4) || !aligned(v_scale, 16) || (q_scale != nullptr && !aligned(q_scale, 4)))
+    return GQA_ERR_MISALIGNED;
+  st = check_int8kv_lengths(q_len, kv_len);
+  if (st != GQA_OK) return st;
+  const Launch lc = plan_int8kv(q_len);
+  Params p;
+  p.q = static_cast<const uint8_t*>(q);
+  p.qsc = q_scale;
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v_codes);
+  p.bt = nullptr;
+  p.ks = k_scale;
+  p.out = static_cast<uint8_t*>(out);
+  p.num_blocks = 0;
+  p.q_len = q_len;
+  p.kv_len = kv_len;
+  p.n_tblk = lc.n_tblk;
+  p.n_seg = 1;
+  p.n_plain = 0;
+  p.ws_o = nullptr;
+  p.ws_ml = nullptr;
+  p.vs = v_scale;
+  p.v_ld = v_ld;
+  hipLaunchKernelGGL((gqa_prefill_kernel<false, true, kDefaultQB, true>), dim3((unsigned)lc.workgroups),
+                     dim3(lc.threads), 0, static_cast<hipStream_t>(stream), p);
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+int gqa_quantize_v_int8(const void* v, int32_t kv_len, int32_t v_ld, void* v_codes, float* v_scale,
+                        void* stream) {
+  if (kv_len < 0 || kv_len > GQA_MAX_LEN || v_ld < kv_len || v_ld > GQA_MAX_LEN || (v_ld & 15) != 0)
+    return GQA_ERR_BAD_LENGTH;
+  if (v_codes == nullptr || v_scale == nullptr || (kv_len > 0 && v == nullptr)) return GQA_ERR_NULL_ARG;
+  if (!aligned(v, 16) || !aligned(v_codes, 16) || !aligned(v_scale, 4)) return GQA_ERR_MISALIGNED;
+  hipLaunchKernelGGL(quantize_v_kernel, dim3(kHkv * kD / 64), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint8_t*>(v), kv_len, v_ld, static_cast<int8_t*>(v_codes), v_scale);
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
 int gqa_quantize_rows_int8(const void* x, int64_t rows, void* xq, float* scale, void* stream) {

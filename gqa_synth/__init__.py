@@ -44,6 +44,7 @@ class Workload:
     kv_len: int
     paged: bool = False
     int8k: bool = False
+    int8v: bool = False   # INT8 values too (INT8 P·V); implies int8k
     num_blocks: int = 0   # paged only: physical blocks in the cache
     seed: int = 0
 
@@ -70,6 +71,8 @@ WORKLOADS = {
                  seed=10),
     # the INT8-K chunk's shape and inputs (seed 5) with bf16 keys: what INT8 keys save
     11: Workload("bf16k_3072x16384", 3072, 16384, seed=5),
+    # the same chunk with INT8 values as well (INT8 P·V), same inputs
+    12: Workload("int8kv_3072x16384", 3072, 16384, int8k=True, int8v=True, seed=5),
 }
 
 
@@ -145,7 +148,8 @@ def make_workload(w: Workload) -> dict:
 
     Keys: q, k, v (logical bf16), plus for paged workloads block_table (int32),
     k_cache and v_cache (bf16 [num_blocks, 4, 16, 256]).
-    INT8-K workloads return bf16 K here; quantising it is the caller's step.
+    INT8-K (and INT8-value) workloads return bf16 K and V here; quantising them is the
+    caller's step.
     """
     q, k, v, rng = make_qkv(w.q_len, w.kv_len, w.seed)
     out = dict(q=q, k=k, v=v)

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define GQA_ABI_VERSION 4
+#define GQA_ABI_VERSION 5
 #define GQA_NUM_Q_HEADS 24
 #define GQA_NUM_KV_HEADS 4
 #define GQA_HEAD_DIM 256
@@ -52,6 +52,9 @@ extern "C" {
 /* largest accepted q_len / kv_len (keeps every device offset inside int64 and
    every grid inside HIP's limits) */
 #define GQA_MAX_LEN (1 << 24)
+/* longest history gqa_attn_prefill_int8kv accepts: its int32 sums of P and V codes
+   (at most 127 * 127 per key) stay below 2^31 */
+#define GQA_INT8KV_MAX_KV (1 << 17)
 /* bytes of device scratch memory gqa_attn_prefill_noalloc holds per GPU (64 MiB) */
 #define GQA_NOALLOC_SCRATCH_BYTES (64u << 20)
 
@@ -61,8 +64,10 @@ typedef enum gqa_status {
   GQA_ERR_BAD_LENGTH = 2,   /* q_len < 0, kv_len < q_len, a length above GQA_MAX_LEN,
                                rows < 0, or num_blocks too small for kv_len */
   GQA_ERR_MISALIGNED = 3,   /* a tensor pointer is not aligned as documented */
-  GQA_ERR_UNSUPPORTED = 4,  /* a combination this build refuses: none in the library; a
-                               comparison build with 32-key tiles refuses paged INT8 keys */
+  GQA_ERR_UNSUPPORTED = 4,  /* a combination this build refuses: INT8 values over more than
+                               GQA_INT8KV_MAX_KV keys or a paged cache; a comparison build
+                               with 32-key tiles also refuses paged INT8 keys and INT8
+                               values */
   GQA_ERR_HIP = 5,          /* the HIP launch failed */
   GQA_ERR_WORKSPACE = 6,    /* gqa_attn_prefill_ws: workspace NULL or too small */
   GQA_ERR_SCRATCH = 7       /* gqa_attn_prefill_noalloc: the call's KV segments need more
@@ -133,8 +138,8 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v,
  * segments x (rows of the cut token blocks) x 24 x (256 + 2) floats.
  * With INT8 keys every segment quantises its query rows itself (same codes).
  *
- * paged, int8k: 0 or 1. Pure host function. Returns 0 for arguments
- * gqa_attn_prefill_ws would refuse.
+ * paged, int8k: 0 or 1 (int8k = 2, INT8 values, gives 0: that call never splits).
+ * Pure host function. Returns 0 for arguments gqa_attn_prefill_ws would refuse.
  */
 size_t gqa_attn_prefill_workspace_size(int32_t q_len, int32_t kv_len, int paged,
                                        int int8k);
@@ -212,6 +217,65 @@ int gqa_attn_prefill_qint8(const void* q_codes, const float* q_scale, const void
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gqa_attn_prefill_int8kv - attention with INT8 keys, INT8 values and an INT8 P·V product.
+ *
+ * "gfx936 DCU上实现INT8 QK MMAC" §6 names INT8 PV (V held in INT8) among the pieces of the
+ * pages' final submission and defines nothing more. This call takes the reading whose
+ * result does not depend on how the work is tiled:
+ *   - V codes per (KV head, feature) over the sequence, as gqa_quantize_v_int8 writes
+ *     them: sV[g, f] = max_t |V[t, g, f]| / 127 and Vq = round(V / sV), so one scale per
+ *     feature factors out of the whole key reduction;
+ *   - P codes against each row's exact maximum over its visible keys:
+ *     Pq = round(127 * exp(s - max s)) in [0, 127], the scores s as for INT8 keys (§1);
+ *   - out = sV * sum_j(Pq_j Vq_j) / sum_j Pq_j, both sums exact in int32, the row sum
+ *     from the same codes.
+ * The exponential is the GPU's exp2 in float32, so a P code whose 127 exp(s - max s) lies
+ * within about 1e-3 of k + 1/2 may round either way.
+ * The call first sweeps every visible key for the row maxima, then runs one pass; it
+ * never cuts the history into KV segments and has no decode shape.
+ *
+ * q        bf16 [q_len, 24, 256], quantised per row inside the call as for
+ *          gqa_attn_prefill with INT8 keys; or, when q_scale != NULL, the int8 codes
+ *          written by gqa_quantize_rows_int8 with q_scale float32 [q_len, 24] (bit for bit
+ *          the same result). 16-byte aligned; q_scale 4-byte aligned.
+ * k, k_scale  int8 [kv_len, 4, 256] and float32 [kv_len, 4], as for gqa_attn_prefill
+ *          (contiguous). 16- and 4-byte aligned.
+ * v_codes  int8 [4, 256, v_ld]: code of V[t, g, f] at [g, f, t] (token index fastest);
+ *          positions kv_len .. v_ld - 1 of each row are never used. 16-byte aligned.
+ * v_scale  float32 [4, 256]; 16-byte aligned.
+ * v_ld     tokens per stored row: a multiple of 16, kv_len <= v_ld <= GQA_MAX_LEN.
+ * q_len, kv_len  0 <= q_len <= kv_len <= GQA_INT8KV_MAX_KV; q_len == 0 is a no-op.
+ * out      bf16 [q_len, 24, 256], fully overwritten; 16-byte aligned; must not overlap
+ *          the inputs.
+ *
+ * Returns GQA_OK, GQA_ERR_NULL_ARG, GQA_ERR_BAD_LENGTH (also for a bad v_ld),
+ * GQA_ERR_MISALIGNED, GQA_ERR_UNSUPPORTED (kv_len > GQA_INT8KV_MAX_KV) or GQA_ERR_HIP.
+ */
+int gqa_attn_prefill_int8kv(const void* q, const float* q_scale, const void* k,
+                            const float* k_scale, const void* v_codes, const float* v_scale,
+                            int32_t v_ld, int32_t q_len, int32_t kv_len, void* out,
+                            void* stream);
+
+/*
+ * gqa_quantize_v_int8 - the V producer's quantisation for gqa_attn_prefill_int8kv: the
+ * per-row rule of gqa_quantize_rows_int8 applied to each (KV head, feature) column of V
+ * along the tokens, written feature-major.
+ *
+ * v        bf16 [kv_len, 4, 256]; 16-byte aligned (may be NULL when kv_len == 0).
+ * v_codes  int8 [4, 256, v_ld] output: the code of v[t, g, f] at [g, f, t]; positions
+ *          kv_len .. v_ld - 1 are written as 0. 16-byte aligned.
+ * v_scale  float32 [4, 256] output: s = max_t |v[t, g, f]| / 127 (IEEE division);
+ *          codes clamp(round-half-even(v / s), -127, 127); a zero column gives s = 0 and
+ *          codes 0. 4-byte aligned.
+ * kv_len   0 <= kv_len <= GQA_MAX_LEN; v_ld a multiple of 16 with kv_len <= v_ld <=
+ *          GQA_MAX_LEN.
+ *
+ * Returns GQA_OK, GQA_ERR_NULL_ARG, GQA_ERR_BAD_LENGTH, GQA_ERR_MISALIGNED or GQA_ERR_HIP.
+ */
+int gqa_quantize_v_int8(const void* v, int32_t kv_len, int32_t v_ld, void* v_codes,
+                        float* v_scale, void* stream);
+
+/*
  * gqa_quantize_rows_int8 - the per-row INT8 quantiser of "gfx936 DCU上实现INT8 QK
  * MMAC" §1/§4 as a standalone step (the K-cache producer's quantisation; the
  * attention call applies the same rule to Q internally).
@@ -240,9 +304,10 @@ int gqa_quantize_rows_int8(const void* x, int64_t rows, void* xq, float* scale,
  * the same way the pages' dispatch depends on the real q_len and kv_len of a
  * chunk ("DCU使用技术报告（中篇）" §3, §5).
  *
- * paged, int8k: 0 or 1. Returns the same status codes as gqa_attn_prefill
- * would for these lengths (argument checks only) and GQA_ERR_NULL_ARG when
- * buf is NULL or n is 0.
+ * paged: 0 or 1; int8k: 0 (bf16 keys), 1 (INT8 keys) or 2 (INT8 keys and values:
+ * the launch of gqa_attn_prefill_int8kv, always one segment). Returns the same status
+ * codes as the call would for these lengths (argument checks only) and
+ * GQA_ERR_NULL_ARG when buf is NULL or n is 0.
  */
 int gqa_attn_prefill_plan(int32_t q_len, int32_t kv_len, int paged, int int8k,
                           char* buf, size_t n);

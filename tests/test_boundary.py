@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"gqa_attn_prefill", "gqa_attn_prefill_ws", "gqa_attn_prefill_workspace_size",
             "gqa_attn_prefill_qint8", "gqa_quantize_rows_int8", "gqa_attn_prefill_plan",
-            "gqa_attn_prefill_noalloc",
+            "gqa_attn_prefill_noalloc", "gqa_attn_prefill_int8kv", "gqa_quantize_v_int8",
             "gqa_abi_version", "gqa_status_string"} <= set(names)
     lib = ctypes.CDLL(gqa_build.LIB)
     for n in names:
@@ -54,7 +54,7 @@ def test_probe_library_loads():
 
 
 def test_abi_version_and_status_strings():
-    assert binding.gqa_abi_version() == 4
+    assert binding.gqa_abi_version() == 5
     for s in range(8):
         assert binding.gqa_status_string(s)
     assert binding.gqa_status_string(99) == "unknown status"
@@ -309,3 +309,67 @@ def test_noalloc_refuses_plans_beyond_its_scratch(paged, int8k):
     # argument errors still come first
     assert noalloc_call(5, 4, paged, int8k) == BADLEN
     assert noalloc_call(0, 4, paged, int8k) == OK
+
+
+def call_int8kv(q=16, qs=None, k=16, ks=16, v=16, vs=16, v_ld=16, q_len=4, kv_len=8, out=16):
+    lib = binding.library()
+    vp = ctypes.c_void_p
+    return lib.gqa_attn_prefill_int8kv(vp(q), vp(qs), vp(k), vp(ks), vp(v), vp(vs), v_ld, q_len,
+                                       kv_len, vp(out), None)
+
+
+def test_int8kv_argument_errors_return_before_launch():
+    # q_len == 0 is a no-op whatever the pointers
+    assert call_int8kv(q=None, k=None, ks=None, v=None, vs=None, out=None, q_len=0) == OK
+    assert call_int8kv(q_len=5, kv_len=4) == BADLEN
+    for which in ("q", "k", "ks", "v", "vs", "out"):
+        assert call_int8kv(**{which: None}) == NULL, which
+    # v_ld: a multiple of 16, at least kv_len
+    assert call_int8kv(v_ld=8) == BADLEN
+    assert call_int8kv(v_ld=24) == BADLEN
+    assert call_int8kv(kv_len=40, v_ld=32) == BADLEN
+    assert call_int8kv(v_ld=-16) == BADLEN
+    for which in ("q", "k", "v", "out", "vs"):
+        assert call_int8kv(**{which: 16 + 4}) == MISALIGNED, which
+    assert call_int8kv(ks=16 + 1) == MISALIGNED
+    assert call_int8kv(qs=16 + 2) == MISALIGNED
+    # the int32 sums bound the history
+    lim = binding.INT8KV_MAX_KV
+    assert call_int8kv(q_len=1, kv_len=lim + 1, v_ld=lim + 16) == UNSUPPORTED
+
+
+def test_v_quantizer_argument_checks():
+    lib = binding.library()
+    vp = ctypes.c_void_p
+    q = lib.gqa_quantize_v_int8
+    assert q(vp(16), -1, 16, vp(16), vp(16), None) == BADLEN
+    assert q(vp(16), 20, 16, vp(16), vp(16), None) == BADLEN
+    assert q(vp(16), 8, 24, vp(16), vp(16), None) == BADLEN
+    assert q(None, 8, 16, vp(16), vp(16), None) == NULL
+    assert q(vp(16), 8, 16, None, vp(16), None) == NULL
+    assert q(vp(16), 8, 16, vp(16), None, None) == NULL
+    assert q(vp(16 + 8), 8, 16, vp(16), vp(16), None) == MISALIGNED
+    assert q(vp(16), 8, 16, vp(16 + 4), vp(16), None) == MISALIGNED
+    assert q(vp(16), 8, 16, vp(16), vp(16 + 2), None) == MISALIGNED
+
+
+def test_plan_int8kv():
+    plan = binding.gqa_attn_prefill_plan(3072, 16384, int8k=2)
+    assert "variant=int8kv_contiguous_t32h6_kt64" in plan
+    assert "segments=1" in plan and "workgroups=384" in plan and "workspace_bytes=0" in plan
+    # every q_len runs the prefill shape (there is no decode shape for INT8 values)
+    assert "workgroups=4 " in binding.gqa_attn_prefill_plan(1, 32768, int8k=2)
+    assert binding.gqa_attn_prefill_workspace_size(3072, 16384, int8k=2) == 0
+    with pytest.raises(binding.GqaError):
+        binding.gqa_attn_prefill_plan(1, binding.INT8KV_MAX_KV + 1, int8k=2)
+    with pytest.raises(binding.GqaError):
+        binding.gqa_attn_prefill_plan(16, 64, paged=True, int8k=2)
+
+
+def test_int8kv_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros((4, 24, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.gqa_attn_prefill_int8kv(q, None, None, None, None)
+    with pytest.raises(ValueError):
+        binding.gqa_quantize_v_int8(torch.zeros((8, 4, 256), dtype=torch.bfloat16))

@@ -38,3 +38,25 @@ def errors(out, ref):
     """(max, mean) of |out - ref| over every element."""
     e = np.abs(as_f64(out) - ref)
     return float(e.max()), float(e.mean())
+
+
+def int8kv_code_slack(c, tmax):
+    """How far from a rounding boundary a P code of the INT8-value path must lie for the
+    kernel to round it as the float64 oracle does.
+
+    The kernel forms 127 * 2^(t - max t) in float32: the score t (log2 units) from the
+    int32 dot product times fl(sK * fl(sQ * fl(log2(e) / 16))) (three roundings), the row
+    maximum from the same products, the exponent as one fused multiply-add against
+    fl(max - fl(log2 127)), then the GPU's exp2 (accurate to about one ulp). With T the
+    row's largest |t| the exponent is off by at most 2^-24 (11.1 T + 21), which moves
+    127 * 2^x by a relative ln(2) times that plus 2^-22; the slack below is twice that
+    bound: c * 2^-23 * (8 T + 24). Codes within it of k + 1/2 may round either way; the
+    oracle turns them into a per-element allowance.
+    """
+    return np.asarray(c) * 2.0 ** -23 * (8.0 * np.asarray(tmax)[:, None] + 24.0)
+
+
+def int8kv_excess(out, ref, slack):
+    """Largest |err| - (2e-3 + half a bf16 ulp of ref + the code allowance); <= 0 passes."""
+    e = np.abs(as_f64(out) - ref)
+    return float(np.max(e - (INT8_MAX + half_ulp_bf16(ref) + slack)))
