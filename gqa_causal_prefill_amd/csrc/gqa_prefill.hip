@@ -2062,9 +2062,13 @@ int gqa_attn_prefill_int8kv(const void* q, const float* q_scale, const void* k, 
   p.ws_ml = nullptr;
   p.vs = v_scale;
   p.v_ld = v_ld;
-  hipLaunchKernelGGL((gqa_prefill_kernel<false, true, kDefaultQB, true>), dim3((unsigned)lc.workgroups),
-                     dim3(lc.threads), 0, static_cast<hipStream_t>(stream), p);
-  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+  if constexpr (kKt == 64) {   // the INT8-value kernel is built for 64-key tiles only
+    hipLaunchKernelGGL((gqa_prefill_kernel<false, true, kDefaultQB, true>), dim3((unsigned)lc.workgroups),
+                       dim3(lc.threads), 0, static_cast<hipStream_t>(stream), p);
+    return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+  } else {
+    return GQA_ERR_UNSUPPORTED;
+  }
 }
 
 int gqa_quantize_v_int8(const void* v, int32_t kv_len, int32_t v_ld, void* v_codes, float* v_scale,
