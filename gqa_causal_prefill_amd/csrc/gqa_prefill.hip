@@ -386,25 +386,29 @@ struct ScaleCopy {
 // INT8 values: the producer stores the codes feature-major, [4, 256, ld] with the token
 // index fastest, so a tile (64 keys of all 256 features of KV head g) is one 64-byte run
 // per feature. In LDS each feature f is a 64-byte row; its 16-byte slot s holds, as dwords
-// kb = 0..3, the keys 16 kb + 4 L .. 16 kb + 4 L + 3 with L = s ^ ((f >> 2) & 3). Lane
+// kb = 0..3, the keys 16 kb + 4 L .. 16 kb + 4 L + 3 with L = s ^ ((f >> 1) & 3). Lane
 // (L, c) of the P·V step needs for feature c of a 16-feature block exactly the 16 keys whose
 // scores its S^T registers hold (keys 16 kb + 4 L + r, r = 0..3), in that order: one
-// ds_read_b128 of slot L ^ ((c >> 2) & 3), and the XOR puts the 16 lanes of a lane group
-// in 16 different 16-byte bank groups. A copy instruction fills 4 feature rows (256 B, lane
-// l writing dword l), one dword (4 keys) per lane; wave w copies features 64 w .. 64 w + 63
-// in 16 instructions. Feature 64 w + 4 I + (l >> 4) of instruction I has swizzle I & 3, so
-// a lane needs 4 source offsets. The descriptor covers the wave's 64 rows up to the tile's
-// last key, cut at the end of the array; a tile at or past kv_len has no range at all.
+// ds_read_b128 of slot L ^ ((c >> 1) & 3). A 16-byte read is served 8 lanes at a time
+// from a 128-byte bank row (the K reads' pattern is conflict-free by that rule, and a swizzle
+// on f >> 2 measured 2-way conflicts); rows c = 0..7 of a lane group fall at 64 (c & 1)
+// modulo 128, and the XOR on c >> 1 gives the four rows of each parity four different
+// slots. A copy instruction fills 4 feature rows (256 B, lane l writing dword l), one dword
+// (4 keys) per lane; wave w copies features 64 w .. 64 w + 63 in 16 instructions. Feature
+// 64 w + 4 I + (l >> 4) of instruction I has swizzle (2 I + (l >> 5)) & 3, so a lane needs
+// 2 source offsets, for even and odd I. The descriptor covers the wave's 64 rows up to the
+// tile's last key, cut at the end of the array; a tile at or past kv_len has no range at all.
 struct VtCopy {
   static constexpr int kInsts = 16;
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t lds;   // LDS address of the wave's first feature row in the destination tile
   uint32_t ld;    // bytes between feature rows
 
-  // source offset of lane l for the instructions I with I % 4 == J
-  static __device__ __forceinline__ uint32_t lane_offset(int lane, int J, int ld) {
+  // source offset of lane l for the instructions I with I % 2 == P
+  static __device__ __forceinline__ uint32_t lane_offset(int lane, int P, int ld) {
     const int d = lane & 15;   // destination dword in the feature row: slot d >> 2, key block d & 3
-    return (uint32_t)((lane >> 4) * ld + 16 * (d & 3) + 4 * ((d >> 2) ^ J));
+    const int swz = (2 * P + (lane >> 5)) & 3;
+    return (uint32_t)((lane >> 4) * ld + 16 * (d & 3) + 4 * ((d >> 2) ^ swz));
   }
   __device__ __forceinline__ VtCopy(const Params& p, int g, int kbase, int w, uint32_t lds_tile) {
     const int n = min(max(p.kv_len - kbase, 0), kKt);
@@ -420,8 +424,8 @@ struct VtCopy {
   }
   // the whole offset goes into the lane's offset, which the range check covers
   template <int I>
-  __device__ __forceinline__ void issue(const uint32_t (&vto)[4]) const {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds + I * 256), 4, vto[I & 3] + (4 * I) * ld,
+  __device__ __forceinline__ void issue(const uint32_t (&vto)[2]) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds + I * 256), 4, vto[I & 1] + (4 * I) * ld,
                                              0, 0, 0);
   }
 };
@@ -795,10 +799,10 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   const uint32_t smem_addr = lds_addr(smem);
   const uint32_t sk_addr = smem_addr + kSkOff;   // key-scale ring (INT8 keys)
   const uint32_t kvo[2] = {KCopy::lane_offset(lane, 0), KCopy::lane_offset(lane, kHalves - 1)};
-  uint32_t vvo[INT8V ? 4 : 2];
+  uint32_t vvo[2];
   if constexpr (INT8V) {
-#pragma unroll
-    for (int J = 0; J < 4; ++J) vvo[J] = VtCopy::lane_offset(lane, J, p.v_ld);
+    vvo[0] = VtCopy::lane_offset(lane, 0, p.v_ld);
+    vvo[1] = VtCopy::lane_offset(lane, 1, p.v_ld);
   } else {
     vvo[0] = VCopy::lane_offset(lane, 0);
     vvo[1] = VCopy::lane_offset(lane, kHalves - 1);
@@ -942,9 +946,9 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
-  // INT8 values: lane (L, c) reads slot L ^ ((c >> 2) & 3) of feature row c of each
+  // INT8 values: lane (L, c) reads slot L ^ ((c >> 1) & 3) of feature row c of each
   // 16-feature block (VtCopy)
-  const uint32_t vt8_off = c * kKt + 16 * (L ^ ((c >> 2) & 3));
+  const uint32_t vt8_off = c * kKt + 16 * (L ^ ((c >> 1) & 3));
   const i32x4 ones8 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 
   // ---- accumulators: O^T blocks [feature block db][query block b], row sums ----
