@@ -34,6 +34,8 @@ def load(path):
     vp, i32 = ctypes.c_void_p, ctypes.c_int32
     lib.gqa_attn_prefill.restype = ctypes.c_int
     lib.gqa_attn_prefill.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, vp]
+    lib.gqa_attn_prefill_int8kv.restype = ctypes.c_int
+    lib.gqa_attn_prefill_int8kv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp]
     lib.gqa_attn_prefill_plan.restype = ctypes.c_int
     lib.gqa_attn_prefill_plan.argtypes = [i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_char_p,
                                           ctypes.c_size_t]
@@ -106,3 +108,33 @@ def test_full_size_bitwise_equal(libs):
     a, b = (run(lib, q, k, v, w.kv_len) for lib in libs)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("q_len,kv_len", [(5, 5), (33, 100), (200, 1300), (97, 2113)])
+def test_int8kv_bitwise_equal(libs, q_len, kv_len):
+    """INT8 values: the P codes, the exact row maxima and the int32 sums do not depend on how
+    the columns are grouped, and integer sums are exact in any order, so the two builds
+    agree bit for bit at every history length (short ones included)."""
+    import numpy as np
+    import oracle
+
+    note(f"case invariance int8kv {q_len}x{kv_len}")
+    q, k, v, _ = make_qkv(q_len, kv_len, seed=6200 + kv_len)
+    kq, ks = oracle.quantize_rows_int8(k)
+    vq, vs = oracle.quantize_v_int8(v)
+    ld = (kv_len + 15) // 16 * 16
+    stored = np.zeros((4, 256, ld), np.int8)
+    stored[:, :, :kv_len] = vq
+    q = q.to(DEV)
+    kq, ks = torch.from_numpy(kq).to(DEV), torch.from_numpy(ks).to(DEV)
+    vq, vs = torch.from_numpy(stored).to(DEV), torch.from_numpy(vs).to(DEV)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    outs = []
+    for lib in libs:
+        out = torch.empty_like(q)
+        st = lib.gqa_attn_prefill_int8kv(p(q), None, p(kq), p(ks), p(vq), p(vs), ld, q_len, kv_len,
+                                         p(out), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
