@@ -430,6 +430,38 @@ struct VtCopy {
   }
 };
 
+// ---- phase clock: a measurement build only (-DGQA_PHASE_CLOCK=1 or 2; the library has none of it) ----
+// Each wave adds up the shader cycles (s_memtime) of the phases of its tile loop and reads
+// the 100 MHz real-time counter (s_memrealtime) around the loop, so that cycles over real
+// time give the shader clock under load. Slots per wave: Q·K^T + softmax, P·V, copy wait
+// and barrier (unmasked tiles), unmasked tiles, masked-tile cycles, masked tiles, the
+// INT8-value maximum sweep's cycles and tiles, loop cycles, loop real-time ticks.
+#ifdef GQA_PHASE_CLOCK
+constexpr int kPhaseWaves = 8192 * 4;
+constexpr int kPhaseSlots = 10;
+__device__ unsigned long long phase_clock[kPhaseWaves * kPhaseSlots];
+struct PhaseClock {
+  unsigned long long qk = 0, pv = 0, sync = 0, n = 0, masked = 0, n_masked = 0, sweep = 0, n_sweep = 0,
+                     c0 = 0, r0 = 0;
+  // GQA_PHASE_CLOCK=2 also pins every read in the instruction order (a scheduling barrier on
+  // each side), so the phases are exact for that order, which then differs from the library's
+  static __device__ __forceinline__ unsigned long long cycles() {
+#if GQA_PHASE_CLOCK >= 2
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned long long t = __builtin_readcyclecounter();
+    __builtin_amdgcn_sched_barrier(0);
+    return t;
+#else
+    return __builtin_readcyclecounter();
+#endif
+  }
+  static __device__ __forceinline__ unsigned long long ticks() { return __builtin_amdgcn_s_memrealtime(); }
+};
+#define GQA_PC(...) __VA_ARGS__
+#else
+#define GQA_PC(...)
+#endif
+
 __device__ __forceinline__ void wait_vm_all() {
   // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -751,6 +783,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
   const int c = lane & 15;      // query column (token) inside a 16-column block
   const int tw = w % S::kTokenBlocks;
   const int hw = w / S::kTokenBlocks;
+  GQA_PC(PhaseClock pc;)
 
   // Workgroup id -> (KV head, KV segment, head subset, token block) by unit_of. id % 4 is
   // the KV head, so workgroups dispatched round-robin over the 8 XCDs keep one KV head per
@@ -1147,6 +1180,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     int blk_k = block_of(copy_base(j0 + 2));   // K and scale copies of the current iteration
     // returns true when pass 0 must restart
     auto body = [&](int j, auto mask_c) -> bool {
+      GQA_PC(const unsigned long long tp0 = PhaseClock::cycles();)
       const int kbase = j * kKt;
       const uint8_t* knext = smem + ((j + 1) & 1) * kKTile;             // K(j+1) (stale on the last tile)
       const uint8_t* vcur = smem + kVOff + (j & 1) * kVTile;   // V(j)
@@ -1231,6 +1265,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       };
       half(std::integral_constant<int, 0>{});
       if constexpr (kHalves > 1) half(std::integral_constant<int, 1>{});
+      GQA_PC(const unsigned long long tp1 = PhaseClock::cycles();)
 
       // ---- O^T += V^T(j) · P^T(j); INT8 keys: S(j+1) is scaled between the steps, where
       // the vector ALU has room (the Q·K^T halves above are short on it: half as many
@@ -1285,6 +1320,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
         });
       }
 
+      GQA_PC(const unsigned long long tp2 = PhaseClock::cycles();)
       // Flags are double-buffered by tile parity: the write for tile j + 2 happens only
       // after every wave has passed barrier j + 1, i.e. after it read tile j's slot, so
       // all waves read the same value and leave the loop on the same tile. A wave's
@@ -1298,6 +1334,16 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       }
       wait_vm_all();
       __syncthreads();   // K(j+2), V(j+1) landed; everyone is done with K(j+1) and V(j)
+      GQA_PC(const unsigned long long tp3 = PhaseClock::cycles();
+             if constexpr (decltype(mask_c)::value) {
+               pc.masked += tp3 - tp0;
+               pc.n_masked += 1;
+             } else {
+               pc.qk += tp1 - tp0;
+               pc.pv += tp2 - tp1;
+               pc.sync += tp3 - tp2;
+               pc.n += 1;
+             })
       if (pass == 0) {
         // act on the flags of the tile before (one tile late, so the read is off the
         // critical path; the extra tile's garbage is discarded by the restart)
@@ -1309,9 +1355,18 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     };
     bool restart = false;
     int j = j0;
+    GQA_PC(pc.qk = pc.pv = pc.sync = pc.n = pc.masked = pc.n_masked = 0;
+           pc.c0 = PhaseClock::cycles(); pc.r0 = PhaseClock::ticks();)
     for (; j < n_plain && !restart; ++j) restart = body(j, std::false_type{});
     for (; j < j1 && !restart; ++j) restart = body(j, std::true_type{});
     if (pass == 0 && !restart && flag_seen != 0) restart = true;   // raised on the last tile
+    GQA_PC(if (lane == 0 && blockIdx.x < kPhaseWaves / 4) {
+             unsigned long long* slot = phase_clock + ((size_t)blockIdx.x * 4 + w) * kPhaseSlots;
+             const unsigned long long c1 = PhaseClock::cycles(), r1 = PhaseClock::ticks();
+             slot[0] = pc.qk; slot[1] = pc.pv; slot[2] = pc.sync; slot[3] = pc.n;
+             slot[4] = pc.masked; slot[5] = pc.n_masked; slot[6] = pc.sweep; slot[7] = pc.n_sweep;
+             slot[8] = c1 - pc.c0; slot[9] = r1 - pc.r0;
+           })
     return restart;
   };
 
@@ -1322,6 +1377,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     float lm[QB];
 #pragma unroll
     for (int b = 0; b < QB; ++b) lm[b] = -__builtin_inff();
+    GQA_PC(const unsigned long long ts0 = PhaseClock::cycles();)
     for (int t = 0; t < ntiles; ++t) {
       const int ahead = min(ntiles - 1 - t, kSweepDepth - 1);   // tiles copied after t so far
       if (ahead >= 2)
@@ -1349,6 +1405,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
 #pragma unroll
     for (int b = 0; b < QB; ++b) m[b] = xor32_max(xor16_max(lm[b])) - kLog2Of127;
     __syncthreads();   // every wave is done with the sweep's buffers
+    GQA_PC(pc.sweep = PhaseClock::cycles() - ts0; pc.n_sweep = ntiles;)
     main_pass(std::integral_constant<int, 1>{});
   } else if (main_pass(std::integral_constant<int, 0>{})) {
     // ---- exact column maxima over every visible key (max-only sweep), then pass 1 ----
@@ -1946,6 +2003,16 @@ int scratch_on(hipStream_t stream, void** ptr) {
 }  // namespace
 
 extern "C" {
+
+#ifdef GQA_PHASE_CLOCK
+// the measurement build's per-wave phase clock of the last launch, copied to host memory
+int gqa_phase_clock_read(void* host, size_t bytes) {
+  if (host == nullptr || bytes > sizeof(phase_clock)) return GQA_ERR_BAD_LENGTH;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(phase_clock), bytes, 0, hipMemcpyDeviceToHost) == hipSuccess
+             ? GQA_OK
+             : GQA_ERR_HIP;
+}
+#endif
 
 int gqa_abi_version(void) { return GQA_ABI_VERSION; }
 
