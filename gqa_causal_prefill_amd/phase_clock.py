@@ -49,6 +49,11 @@ def main():
     ap.add_argument("--markdown", default=None, help="also write the table to this file")
     ap.add_argument("--verbose", action="store_true", help="also print per-wave details")
     ap.add_argument("--append", action="store_true", help="append the table to --markdown as a new section")
+    ap.add_argument("--q-len", type=int, nargs="+", default=None,
+                    help="run each workload's kind (contiguous only) at these q_len instead")
+    ap.add_argument("--kv-len", type=int, default=None, help="with --q-len: the kv_len (default the workload's)")
+    ap.add_argument("--unsplit", action="store_true",
+                    help="call gqa_attn_prefill (never cut into KV segments) instead of gqa_attn_prefill_ws")
     args = ap.parse_args()
     sys.path.insert(0, ROOT)
     import numpy as np
@@ -67,8 +72,19 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     rows = []
+    import dataclasses
+    runs = []
     for wl in args.workloads:
         w = WORKLOADS[wl]
+        if args.q_len:
+            if w.paged:
+                raise SystemExit("--q-len takes contiguous workloads")
+            for ql in args.q_len:
+                kv = args.kv_len or w.kv_len
+                runs.append((wl, dataclasses.replace(w, name=f"{w.name.split('_')[0]}_{ql}x{kv}", q_len=ql, kv_len=kv)))
+        else:
+            runs.append((wl, w))
+    for wl, w in runs:
         if w.paged and w.int8k:
             raise SystemExit("paged INT8 workloads are not covered by this runner")
         print(f"phase_clock: workload {wl} {w.name}", file=sys.stderr, flush=True)
@@ -96,7 +112,10 @@ def main():
             ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
 
             def step():
-                gqa.gqa_attn_prefill_ws(q, k, v, out=out, workspace=ws, stream=stream, **kw)
+                if args.unsplit:
+                    gqa.gqa_attn_prefill(q, k, v, out=out, stream=stream, **kw)
+                else:
+                    gqa.gqa_attn_prefill_ws(q, k, v, out=out, workspace=ws, stream=stream, **kw)
         t = time.time()
         while time.time() - t < 0.3:
             for _ in range(4):
@@ -110,6 +129,8 @@ def main():
         ms = e0.elapsed_time(e1)
         plan = gqa.gqa_attn_prefill_plan(w.q_len, w.kv_len, w.paged, 2 if w.int8v else int(w.int8k))
         nwg = int(dict(x.split("=") for x in plan.split())["workgroups"])
+        if args.unsplit and not w.int8v:   # one workgroup per (KV head, token block)
+            nwg = 4 * ((w.q_len + 31) // 32) if w.q_len > 4 else 4 * ((w.q_len + 3) // 4)
         buf = np.zeros(nwg * 4 * SLOTS, dtype=np.uint64)
         st = lib.gqa_phase_clock_read(buf.ctypes.data_as(ctypes.c_void_p), buf.nbytes)
         if st != 0:
@@ -121,7 +142,7 @@ def main():
         inside = (p[:, 0] + p[:, 1] + p[:, 2] + p[:, 4]).sum() / p[:, 8].sum()
         clock = p[:, 8].sum() / (p[:, 9].sum() / REALTIME_HZ) / 1e9
         sweep = p[:, 6].sum() / p[:, 7].sum() if p[:, 7].sum() > 0 else None
-        rows.append(dict(wl=wl, name=w.name, ms=ms, qk=per[0], pv=per[1], sync=per[2], tile=sum(per),
+        rows.append(dict(wl=wl, name=w.name if args.q_len else NAMES.get(wl, w.name), wgs=nwg, ms=ms, qk=per[0], pv=per[1], sync=per[2], tile=sum(per),
                          loop_tile=loop_tile, inside=inside,
                          masked=p[:, 4].sum() / max(p[:, 5].sum(), 1), sweep=sweep, clock=clock,
                          span=p[:, 9].max() / REALTIME_HZ * 1e3, tiles=n / (nwg * 4)))
@@ -143,12 +164,23 @@ def main():
         name = os.path.basename(args.library)[len("libgqa_prefill_"):-len(".so")]
         level = {"phase": 1, "phase2": 2}.get(name, 1)
         cmd = "python -m gqa_causal_prefill_amd.phase_clock --workloads " + " ".join(map(str, args.workloads))
+        if args.q_len:
+            cmd += " --q-len " + " ".join(map(str, args.q_len)) + (f" --kv-len {args.kv_len}" if args.kv_len else "")
+        if args.unsplit:
+            cmd += " --unsplit"
+
         if name != "phase":
             cmd += f" --library gqa_causal_prefill_amd/variants/libgqa_prefill_{name}.so"
         title = ("counter reads where the library's instruction order puts them" if level == 1 else
                  "every counter read pinned in the instruction order")
+        note = []
+        if args.q_len and args.unsplit:
+            title += ", grids of fewer workgroups"
+            note = [f"Each workload's kind at q_len {', '.join(map(str, args.q_len))} over the same keys, called without KV segments",
+                    "(`gqa_attn_prefill`): 4 workgroups per 32 query tokens, at most one per CU, so grids of 256 and",
+                    "more keep every CU busy and smaller ones leave CUs idle.", ""]
         md = ([] if args.append else ["# Shader cycles per loop phase and the shader clock under load", ""]) + [
-              f"## -DGQA_PHASE_CLOCK={level}: {title}", "",
+              f"## -DGQA_PHASE_CLOCK={level}: {title}", ""] + note + [
               "Repository root, one MI355X; the measurement build of the library (its source with the phase clock",
               f"compiled in; the library's own machine code has none of it):", "", "```",
               f"python -c 'from gqa_causal_prefill_amd import build; build.build_variant(\"{name}\", [\"-DGQA_PHASE_CLOCK={level}\"])'",
@@ -159,11 +191,11 @@ def main():
               "counter reads at the phase boundaries of the unmasked tiles; the compiler moves instructions across such",
               "reads, so they hold only the share of the loop's cycles given in the next column. Shader clock: loop cycles",
               "over loop time from the 100 MHz `s_memrealtime` counter.", "",
-              "| workload | launch ms | loop cycles per tile | share in timed phases | Q·K^T + softmax | P·V | copy wait + barrier | max sweep per tile | shader clock GHz |",
-              "|---|---|---|---|---|---|---|---|---|"]
+              "| workload | workgroups | launch ms | loop cycles per tile | share in timed phases | Q·K^T + softmax | P·V | copy wait + barrier | max sweep per tile | shader clock GHz |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
         for r in rows:
             sweep = "" if r["sweep"] is None else f"{r['sweep']:.0f}"
-            md.append(f"| {NAMES.get(r['wl'], r['name'])} | {r['ms']:.4f} | {r['loop_tile']:.0f} | {100 * r['inside']:.0f}% | "
+            md.append(f"| {r['name']} | {r['wgs']} | {r['ms']:.4f} | {r['loop_tile']:.0f} | {100 * r['inside']:.0f}% | "
                       f"{r['qk']:.0f} | {r['pv']:.0f} | {r['sync']:.0f} | {sweep} | {r['clock']:.3f} |")
         with open(args.markdown, "a" if args.append else "w") as f:
             f.write(("\n" if args.append else "") + "\n".join(md) + "\n")
