@@ -624,15 +624,19 @@ __device__ __forceinline__ void vt_issue_step(VtFrag& f, const uint32_t (&vbase)
 // into the assembly, so the hazards it would otherwise cover are covered here:
 //  * an MFMA may read a VGPR only 2 wait states after a vector ALU instruction wrote
 //    it: FIRST marks a tile's first MFMA on each P register (P is written by the
-//    vector ALU), and the assembly then starts with s_nop 1;
+//    vector ALU), and the assembly then starts with s_nop 1. That statement also lists P
+//    as an operand it rewrites (it does not), so that every other reader of P depends on
+//    it and the compiler cannot move one ahead of it; without this it reorders the
+//    independent statements of a tile's second key half and puts another before the
+//    first, one wait state after the conversion that wrote P;
 //  * V^T fragments come from LDS reads whose wait precedes the call;
 //  * consecutive MFMAs on the same accumulator need no wait states;
 //  * vector ALU accesses to the accumulators (zeroing, the epilogue) are separated
 //    from the MFMAs by agpr_fence below.
 template <bool FIRST>
-__device__ __forceinline__ void mfma_pv(f32x4& acc, const bf16x8& v, const bf16x8& p) {
+__device__ __forceinline__ void mfma_pv(f32x4& acc, const bf16x8& v, bf16x8& p) {
   if constexpr (FIRST)
-    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %2, %1, %0" : "+a"(acc), "+v"(p) : "v"(v));
   else
     asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
 }
@@ -656,24 +660,65 @@ __device__ __forceinline__ void agpr_fence(T (&o)[16][QB]) {
       if (db != 0 || b != 0) asm volatile("" : "+a"(o[db][b]));
 }
 
+// mfma_pv carrying one to three 32-bit registers through the statement as operands the
+// instruction does not touch. Vector work that reads a carried register after the
+// statement, or whose result a later statement carries, stays between the two statements:
+// the compiler orders them by these operands, and tracks the hazards of that vector work
+// itself, since it is not inside the assembly.
+template <bool FIRST>
+__device__ __forceinline__ void mfma_pv_carry(f32x4& acc, const bf16x8& v, bf16x8& p, uint32_t& a) {
+  if constexpr (FIRST)
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o]"
+        : [o] "+a"(acc), [p] "+v"(p), "+v"(a) : [v] "v"(v));
+  else
+    asm("v_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o]" : [o] "+a"(acc), "+v"(a) : [v] "v"(v), [p] "v"(p));
+}
+template <bool FIRST>
+__device__ __forceinline__ void mfma_pv_carry(f32x4& acc, const bf16x8& v, bf16x8& p, uint32_t& a,
+                                              uint32_t& b) {
+  if constexpr (FIRST)
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o]"
+        : [o] "+a"(acc), [p] "+v"(p), "+v"(a), "+v"(b) : [v] "v"(v));
+  else
+    asm("v_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o]"
+        : [o] "+a"(acc), "+v"(a), "+v"(b) : [v] "v"(v), [p] "v"(p));
+}
+template <bool FIRST>
+__device__ __forceinline__ void mfma_pv_carry(f32x4& acc, const bf16x8& v, bf16x8& p, uint32_t& a,
+                                              uint32_t& b, uint32_t& c) {
+  if constexpr (FIRST)
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o]"
+        : [o] "+a"(acc), [p] "+v"(p), "+v"(a), "+v"(b), "+v"(c) : [v] "v"(v));
+  else
+    asm("v_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o]"
+        : [o] "+a"(acc), "+v"(a), "+v"(b), "+v"(c) : [v] "v"(v), [p] "v"(p));
+}
+
+// Step N of P·V: the MFMA statements go through `mf`, called with the statement's index
+// in the tile (N * QB (* 2 with the low part) + its place in the step), whether it is the
+// first on its P register, and the operands.
 template <int N, int QB, bool SPLIT>
 struct PvStep {
-  template <class Extra>
+  template <class Extra, class Mf>
   static __device__ __forceinline__ void run(VtFrag (&vf)[kVtDepth + 1], const uint32_t (&vbase)[4],
-                                             const bf16x8 (&ph)[QB][2], const bf16x8 (&pl)[QB][2],
+                                             bf16x8 (&ph)[QB][2], bf16x8 (&pl)[QB][2],
                                              const bf16x8& ones, f32x4 (&o)[16][QB],
-                                             f32x4 (&lacc)[QB], Extra&& extra) {
+                                             f32x4 (&lacc)[QB], Extra&& extra, Mf&& mf) {
     constexpr int ks = N >> 4, db = N & 15;
+    constexpr int kMf = SPLIT ? 2 : 1;
     extra(std::integral_constant<int, N>{});
     constexpr int kAhead = (kPvSteps - 1 - N) < kVtDepth ? (kPvSteps - 1 - N) : kVtDepth;  // steps in flight after N
     if constexpr (N + kVtDepth < kPvSteps) vt_issue_step<N + kVtDepth>(vf[(N + kVtDepth) % (kVtDepth + 1)], vbase);
     vt_wait<2 * kAhead>(vf[N % (kVtDepth + 1)]);
     const bf16x8 v = vt_value(vf[N % (kVtDepth + 1)]);
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      mfma_pv<db == 0>(o[db][b], v, ph[b][ks]);
-      if constexpr (SPLIT) mfma_pv<db == 0>(o[db][b], v, pl[b][ks]);
-    }
+    static_for<0, QB>([&](auto bc) {
+      constexpr int b = decltype(bc)::value;
+      mf(std::integral_constant<int, (N * QB + b) * kMf>{}, std::bool_constant<db == 0>{}, o[db][b], v,
+         ph[b][ks]);
+      if constexpr (SPLIT)
+        mf(std::integral_constant<int, (N * QB + b) * kMf + 1>{}, std::bool_constant<db == 0>{}, o[db][b], v,
+           pl[b][ks]);
+    });
     if constexpr (db == 0) {
       // row sums from the same bf16 P the P·V product uses
 #pragma unroll
@@ -683,7 +728,7 @@ struct PvStep {
           lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl[b][ks], lacc[b], 0, 0, 0);
       }
     }
-    if constexpr (N + 1 < kPvSteps) PvStep<N + 1, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc, extra);
+    if constexpr (N + 1 < kPvSteps) PvStep<N + 1, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc, extra, mf);
   }
 };
 
@@ -692,9 +737,9 @@ struct PvStep {
 // step is one read and QB MFMAs of v_mfma_i32_16x16x64_i8 over the whole 64-key tile; the
 // same hazards as mfma_pv apply (FIRST: P was written by the vector ALU).
 template <bool FIRST>
-__device__ __forceinline__ void mfma_pv_i8(i32x4& acc, const i32x4& v, const i32x4& p) {
+__device__ __forceinline__ void mfma_pv_i8(i32x4& acc, const i32x4& v, i32x4& p) {
   if constexpr (FIRST)
-    asm("s_nop 1\n\tv_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
+    asm("s_nop 1\n\tv_mfma_i32_16x16x64_i8 %0, %2, %1, %0" : "+a"(acc), "+v"(p) : "v"(v));
   else
     asm("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
 }
@@ -711,7 +756,7 @@ struct PvStepI8 {
   static constexpr int kSteps = kD / 16;
   template <class Extra>
   static __device__ __forceinline__ void run(u32x4 (&vf)[kVtDepth + 1], uint32_t vbase,
-                                             const i32x4 (&pq)[QB], const i32x4& ones,
+                                             i32x4 (&pq)[QB], const i32x4& ones,
                                              i32x4 (&o)[16][QB], i32x4 (&lacc)[QB], Extra&& extra) {
     extra(std::integral_constant<int, N>{});
     constexpr int kAhead = (kSteps - 1 - N) < kVtDepth ? (kSteps - 1 - N) : kVtDepth;
@@ -1030,9 +1075,9 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     f32x4 skv = __builtin_bit_cast(f32x4, sr[kb]);
     // Empty volatile statements on the operand and on the result hold this unit's
     // conversion and scaling at the P·V step that calls it: volatile statements keep
-    // their order among themselves and the P·V MFMAs are volatile statements too.
-    // Without them the compiler sinks all of a tile's scaling past the tile barrier
-    // (the restart exit does not need it), where it runs with no MFMA to overlap.
+    // their order among themselves, and each step's LDS wait is one. Without them the
+    // compiler sinks all of a tile's scaling past the tile barrier (the restart exit
+    // does not need it), where it runs with no MFMA to overlap.
     if constexpr (decltype(minus_m_c)::value) asm volatile("" : "+v"(sacc[b][kb]), "+v"(skv));
     f32x4 y;
 #pragma unroll
@@ -1305,19 +1350,57 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
         static_for<0, kVtDepth>([&](auto nc) {   // the first kVtDepth steps' reads
           vt_issue_step<decltype(nc)::value>(vf[decltype(nc)::value], vbase);
         });
-        PvStep<0, QB, SPLIT>::run(vf, vbase, ph, pl, ones, o, lacc, [&](auto nc) {
-          if constexpr (INT8K) {
-            constexpr int N = decltype(nc)::value;
-            // at step 1 only the 2 kVtDepth reads of steps 1 .. kVtDepth are younger
-            // than the scale reads: the wait costs nothing and marks them valid
-            if constexpr (N == 1) lds_wait4<2 * kVtDepth>(sr[0], sr[1], sr[2], sr[3]);
-            if constexpr (N >= 2 && N % 2 == 0 && (N - 2) / 2 < kKb * QB) {
-              constexpr int u = (N - 2) / 2;
-              scale_unit(std::integral_constant<int, u / QB>{}, std::integral_constant<int, u % QB>{}, sr,
-                         std::true_type{});
-            }
-          }
-        });
+        // INT8 keys: the scores of S(j+1) are turned into exponents y - m one at a time
+        // between the P·V MFMAs (the arithmetic of scale_unit): score i is converted and
+        // scaled after statement kAt(i), which carries its int32 and its key scale, and its
+        // result is carried by the next statement; from step 2 on (the scale reads are
+        // waited for at step 1), spread evenly over the tile's statements. Whole 4-score
+        // units at every other step, held there by empty volatile statements, measured
+        // 1.4-3% slower.
+        constexpr int kStmts = kPvSteps * QB * (SPLIT ? 2 : 1);
+        constexpr int kFirst = 2 * QB * (SPLIT ? 2 : 1);
+        constexpr int kScores = 4 * kKb * QB;
+        static_assert(kStmts - 1 - kFirst >= kScores, "one score per MFMA statement at most");
+        constexpr auto kAt = [](int i) { return kFirst + (i * (kStmts - 1 - kFirst)) / kScores; };
+        constexpr auto score_after = [kAt](int k) {
+          for (int i = 0; i < kScores; ++i)
+            if (kAt(i) == k) return i;
+          return -1;
+        };
+        PvStep<0, QB, SPLIT>::run(
+            vf, vbase, ph, pl, ones, o, lacc,
+            [&](auto nc) {
+              // at step 1 only the 2 kVtDepth reads of steps 1 .. kVtDepth are younger
+              // than the scale reads: the wait costs nothing and marks them valid
+              if constexpr (INT8K && decltype(nc)::value == 1) lds_wait4<2 * kVtDepth>(sr[0], sr[1], sr[2], sr[3]);
+            },
+            [&](auto kc, auto first_c, f32x4& acc, const bf16x8& v, bf16x8& pp) {
+              constexpr bool kF = decltype(first_c)::value;
+              constexpr int k = decltype(kc)::value;
+              constexpr int is = INT8K ? score_after(k) : -1;       // starts after this statement
+              constexpr int ie = INT8K ? score_after(k - 1) : -1;   // result carried here
+              if constexpr (is < 0 && ie < 0) {
+                mfma_pv<kF>(acc, v, pp);
+              } else {
+                constexpr int us = is < 0 ? 0 : is / 4, ue = ie < 0 ? 0 : ie / 4;
+                constexpr int kbs = us / QB, bs = us % QB, rs = (is < 0 ? 0 : is) % 4;
+                constexpr int kbe = ue / QB, be = ue % QB, re = (ie < 0 ? 0 : ie) % 4;
+                uint32_t x = sacc[bs][kbs][rs], sk = sr[kbs][rs], y = sacc[be][kbe][re];
+                if constexpr (is >= 0 && ie >= 0)
+                  mfma_pv_carry<kF>(acc, v, pp, x, sk, y);
+                else if constexpr (is >= 0)
+                  mfma_pv_carry<kF>(acc, v, pp, x, sk);
+                else
+                  mfma_pv_carry<kF>(acc, v, pp, y);
+                if constexpr (ie >= 0) sacc[be][kbe][re] = y;
+                if constexpr (is >= 0) {
+#pragma clang fp contract(off)
+                  sr[kbs][rs] = sk;
+                  const float t = __builtin_bit_cast(float, sk) * qs[bs];
+                  sacc[bs][kbs][rs] = __builtin_bit_cast(int, __builtin_fmaf((float)(int)x, t, -m[bs]));
+                }
+              }
+            });
       }
 
       GQA_PC(const unsigned long long tp2 = PhaseClock::cycles();)
