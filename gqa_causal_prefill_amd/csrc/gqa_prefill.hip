@@ -1674,6 +1674,7 @@ __global__ __launch_bounds__(kThreads, 1) void gqa_prefill_kernel(const Params p
 // meet in LDS. Loads are unconditional (the workspace holds n_seg full rows) and an
 // empty segment's contribution is dropped by a select, so whatever its O_s holds never
 // reaches the result.
+constexpr int kMergeBatch = 16;   // segments per wave loaded at once (up to 64 segments)
 __global__ __launch_bounds__(256) void merge_segments_kernel(const float* ws_o, const float* ws_ml,
                                                              int n_seg, int64_t rows, uint8_t* out) {
   const int64_t row = blockIdx.x;
@@ -1681,20 +1682,48 @@ __global__ __launch_bounds__(256) void merge_segments_kernel(const float* ws_o, 
   const int f = blockIdx.y * 64 + lane;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml);
   float mmax = -__builtin_inff();
-  for (int sg = lane; sg < n_seg; sg += 64) {
-    const float2 v = ml[sg * rows + row];
-    mmax = v.y > 0.0f ? fmaxf(mmax, v.x) : mmax;
-  }
-  for (int x = 32; x >= 1; x >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, x));
   float acc = 0.0f, lsum = 0.0f;
+  if (n_seg <= 4 * kMergeBatch) {
+    // every load of the workgroup issued before any arithmetic (one round trip to memory
+    // instead of one per batch of the loop below), then the same sums in the same order;
+    // indices past n_seg load segment 0 and are not used
+    float2 mv[kMergeBatch];
+    float ov[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int sg = wv + 4 * i < n_seg ? wv + 4 * i : 0;
+      mv[i] = ml[sg * rows + row];
+      ov[i] = ws_o[(size_t)(sg * rows + row) * kD + f];
+    }
+    const float2 vm = ml[(lane < n_seg ? lane : 0) * rows + row];
+    if (lane < n_seg) mmax = vm.y > 0.0f ? fmaxf(mmax, vm.x) : mmax;
+    for (int x = 32; x >= 1; x >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, x));
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (wv + 4 * i < n_seg) {
+        const float2 v = mv[i];
+        const float o = ov[i];
+        const bool used = v.y > 0.0f;
+        const float wgt = __builtin_amdgcn_exp2f(v.x - mmax);
+        acc += used ? wgt * o : 0.0f;
+        lsum += used ? wgt * v.y : 0.0f;
+      }
+    }
+  } else {
+    for (int sg = lane; sg < n_seg; sg += 64) {
+      const float2 v = ml[sg * rows + row];
+      mmax = v.y > 0.0f ? fmaxf(mmax, v.x) : mmax;
+    }
+    for (int x = 32; x >= 1; x >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, x));
 #pragma unroll 4
-  for (int sg = wv; sg < n_seg; sg += 4) {
-    const float2 v = ml[sg * rows + row];
-    const float o = ws_o[(size_t)(sg * rows + row) * kD + f];
-    const bool used = v.y > 0.0f;
-    const float wgt = __builtin_amdgcn_exp2f(v.x - mmax);
-    acc += used ? wgt * o : 0.0f;
-    lsum += used ? wgt * v.y : 0.0f;
+    for (int sg = wv; sg < n_seg; sg += 4) {
+      const float2 v = ml[sg * rows + row];
+      const float o = ws_o[(size_t)(sg * rows + row) * kD + f];
+      const bool used = v.y > 0.0f;
+      const float wgt = __builtin_amdgcn_exp2f(v.x - mmax);
+      acc += used ? wgt * o : 0.0f;
+      lsum += used ? wgt * v.y : 0.0f;
+    }
   }
   __shared__ float part[4][64];
   __shared__ float lpart[4];
