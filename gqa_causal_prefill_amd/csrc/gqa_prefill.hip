@@ -636,7 +636,7 @@ __device__ __forceinline__ void vt_issue_step(VtFrag& f, const uint32_t (&vbase)
 template <bool FIRST>
 __device__ __forceinline__ void mfma_pv(f32x4& acc, const bf16x8& v, bf16x8& p) {
   if constexpr (FIRST)
-    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %2, %1, %0" : "+a"(acc), "+v"(p) : "v"(v));
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %2, %1, %0 ; carry %1" : "+a"(acc), "+v"(p) : "v"(v));
   else
     asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
 }
@@ -661,37 +661,38 @@ __device__ __forceinline__ void agpr_fence(T (&o)[16][QB]) {
 }
 
 // mfma_pv carrying one to three 32-bit registers through the statement as operands the
-// instruction does not touch. Vector work that reads a carried register after the
+// instruction does not touch (named in an assembly comment, for the ISA check of the
+// package). Vector work that reads a carried register after the
 // statement, or whose result a later statement carries, stays between the two statements:
 // the compiler orders them by these operands, and tracks the hazards of that vector work
 // itself, since it is not inside the assembly.
 template <bool FIRST>
 __device__ __forceinline__ void mfma_pv_carry(f32x4& acc, const bf16x8& v, bf16x8& p, uint32_t& a) {
   if constexpr (FIRST)
-    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o]"
-        : [o] "+a"(acc), [p] "+v"(p), "+v"(a) : [v] "v"(v));
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o] ; carry %[p] %[ca]"
+        : [o] "+a"(acc), [p] "+v"(p), [ca] "+v"(a) : [v] "v"(v));
   else
-    asm("v_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o]" : [o] "+a"(acc), "+v"(a) : [v] "v"(v), [p] "v"(p));
+    asm("v_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o] ; carry %[ca]" : [o] "+a"(acc), [ca] "+v"(a) : [v] "v"(v), [p] "v"(p));
 }
 template <bool FIRST>
 __device__ __forceinline__ void mfma_pv_carry(f32x4& acc, const bf16x8& v, bf16x8& p, uint32_t& a,
                                               uint32_t& b) {
   if constexpr (FIRST)
-    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o]"
-        : [o] "+a"(acc), [p] "+v"(p), "+v"(a), "+v"(b) : [v] "v"(v));
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o] ; carry %[p] %[ca] %[cb]"
+        : [o] "+a"(acc), [p] "+v"(p), [ca] "+v"(a), [cb] "+v"(b) : [v] "v"(v));
   else
-    asm("v_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o]"
-        : [o] "+a"(acc), "+v"(a), "+v"(b) : [v] "v"(v), [p] "v"(p));
+    asm("v_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o] ; carry %[ca] %[cb]"
+        : [o] "+a"(acc), [ca] "+v"(a), [cb] "+v"(b) : [v] "v"(v), [p] "v"(p));
 }
 template <bool FIRST>
 __device__ __forceinline__ void mfma_pv_carry(f32x4& acc, const bf16x8& v, bf16x8& p, uint32_t& a,
                                               uint32_t& b, uint32_t& c) {
   if constexpr (FIRST)
-    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o]"
-        : [o] "+a"(acc), [p] "+v"(p), "+v"(a), "+v"(b), "+v"(c) : [v] "v"(v));
+    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o] ; carry %[p] %[ca] %[cb] %[cc]"
+        : [o] "+a"(acc), [p] "+v"(p), [ca] "+v"(a), [cb] "+v"(b), [cc] "+v"(c) : [v] "v"(v));
   else
-    asm("v_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o]"
-        : [o] "+a"(acc), "+v"(a), "+v"(b), "+v"(c) : [v] "v"(v), [p] "v"(p));
+    asm("v_mfma_f32_16x16x32_bf16 %[o], %[v], %[p], %[o] ; carry %[ca] %[cb] %[cc]"
+        : [o] "+a"(acc), [ca] "+v"(a), [cb] "+v"(b), [cc] "+v"(c) : [v] "v"(v), [p] "v"(p));
 }
 
 // Registers one P·V MFMA statement carries for the INT8-key scaling (at most 3): a
@@ -790,7 +791,7 @@ struct PvStep {
 template <bool FIRST>
 __device__ __forceinline__ void mfma_pv_i8(i32x4& acc, const i32x4& v, i32x4& p) {
   if constexpr (FIRST)
-    asm("s_nop 1\n\tv_mfma_i32_16x16x64_i8 %0, %2, %1, %0" : "+a"(acc), "+v"(p) : "v"(v));
+    asm("s_nop 1\n\tv_mfma_i32_16x16x64_i8 %0, %2, %1, %0 ; carry %1" : "+a"(acc), "+v"(p) : "v"(v));
   else
     asm("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
 }
@@ -1132,7 +1133,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
     // writes them may still be in flight, and a statement that lists them as outputs would
     // hide that write from the compiler, which then omits the MFMA's wait states before
     // the conversion reads them.
-    if constexpr (decltype(minus_m_c)::value) asm volatile("" : "+v"(skv));
+    if constexpr (decltype(minus_m_c)::value) asm volatile("; hold %0" : "+v"(skv));
     f32x4 y;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1141,7 +1142,7 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
       else
         y[r] = (float)sacc[b][kb][r] * (skv[r] * qs[b]);
     }
-    if constexpr (decltype(minus_m_c)::value) asm volatile("" : "+v"(y));
+    if constexpr (decltype(minus_m_c)::value) asm volatile("; hold %0" : "+v"(y));
     sacc[b][kb] = __builtin_bit_cast(Acc, y);
   };
   // the whole tile at once (outside the pipelined loop)
