@@ -695,11 +695,12 @@ __device__ __forceinline__ void mfma_pv_carry(f32x4& acc, const bf16x8& v, bf16x
         : [o] "+a"(acc), [ca] "+v"(a), [cb] "+v"(b), [cc] "+v"(c) : [v] "v"(v), [p] "v"(p));
 }
 
-// Registers one P·V MFMA statement carries for the INT8-key scaling (at most 3): a
-// score's key scale (SK), float(S) (C), the product of the scales (T) or the finished
-// exponent (Y).
+// Registers one P·V MFMA statement carries for the scaling of the next tile's scores
+// placed between the statements (at most 3): a score's key scale (SK), float(S) (C), the
+// product of the scales (T), the finished exponent (Y) or, with bf16 keys, the maximum of
+// the score's column (M).
 struct CarryPlan {
-  enum { kSK, kC, kT, kY };
+  enum { kSK, kC, kT, kY, kM };
   int n = 0;
   int kind[3] = {0, 0, 0};
   int score[3] = {0, 0, 0};
@@ -741,6 +742,42 @@ struct ScaleSchedule {
       if (gf > gc && (gc + 1 == k || (gf > gc + 1 && gf == k))) add(CarryPlan::kC, i);
       if (gf > gm && (gm + 1 == k || (gf > gm + 1 && gf == k))) add(CarryPlan::kT, i);
       if (gf + 1 == k) add(CarryPlan::kY, i);
+    }
+    return cp;
+  }
+};
+
+// Placement of the bf16-key exponent FMAs of the next tile's first key half (one a
+// score) among the last TAIL gaps of a tile's STMTS P·V MFMA statements (gap g follows
+// statement g), at most two a gap: after the last V reads those MFMAs run back to back
+// and leave the vector ALU idle. Score i's FMA is held after statement g by carrying its
+// column's maximum through g (the score itself, written by a Q·K^T MFMA, is never
+// carried) and before statement g + 1 by carrying its result through g + 1.
+template <int STMTS, int TAIL, int SCORES>
+struct ExpSchedule {
+  static constexpr int kScores = SCORES;
+  static constexpr int kFirst = STMTS - 1 - TAIL;
+  static_assert(kFirst >= 0 && 2 * TAIL >= kScores, "room for the FMAs, two a gap");
+  static constexpr int gap(int i) { return kFirst + (i * TAIL) / kScores; }
+  static constexpr int first_op(int g) {
+    int i = 0;
+    while (i < kScores && gap(i) < g) ++i;
+    return i;
+  }
+  static constexpr CarryPlan carries(int k) {
+    CarryPlan cp;
+    auto add = [&cp](int kind, int i) {
+      cp.kind[cp.n] = kind;
+      cp.score[cp.n] = i;
+      ++cp.n;
+    };
+    int last_u = -1;   // one maximum per 4-score unit (the unit's scores share a column)
+    for (int i = 0; i < kScores; ++i) {
+      if (gap(i) == k && i / 4 != last_u) {
+        add(CarryPlan::kM, i);
+        last_u = i / 4;
+      }
+      if (gap(i) + 1 == k) add(CarryPlan::kY, i);
     }
     return cp;
   }
@@ -1171,11 +1208,21 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
           for (int r = 0; r < 4; ++r) y[r] = y[r] - m[b];
           sacc[b][kb] = __builtin_bit_cast(Acc, y);
         }
+    } else {   // bf16 keys: the first key half's exponents s * log2(e)/16 - m, which the
+               // tile loop forms for the next tile during the P·V steps
+#pragma clang fp contract(off)
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)   // key blocks 0, 1
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sacc[b][kb][r] = __builtin_fmaf(sacc[b][kb][r], kLog2eOver16, -m[b]);
     }
   };
   // scores of key blocks 2h, 2h + 1 (keys kbase + 32 h .. + 31) from sacc, in log2 units
-  // once multiplied by scale[b] (bf16: raw dot products; INT8 keys: already scaled),
-  // causal mask applied. sc[b][e]: e = 0..3 keys 32 h + 4 L + e, e = 4..7 keys 32 h + 16 + 4 L + e - 4
+  // once multiplied by scale[b] (bf16: raw dot products, but inside the tile loop the
+  // first key half already holds its exponents; INT8 keys: already scaled), causal mask
+  // applied. sc[b][e]: e = 0..3 keys 32 h + 4 L + e, e = 4..7 keys 32 h + 16 + 4 L + e - 4
   auto half_scores = [&](auto mask_c, int kbase, int h, float (&sc)[QB][8], float (&scale)[QB]) {
     constexpr bool kMask = decltype(mask_c)::value;
     if constexpr (!INT8K) {
@@ -1333,10 +1380,10 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
         constexpr int H = decltype(hc)::value;
         float sc[QB][8], scale[QB];
         half_scores(mask_c, kbase, H, sc, scale);
-        if constexpr (!INT8K) {
-          // bf16 keys: the exponent s * log2(e)/16 - m at once, reading the accumulators
-          // before this half's MFMAs reuse them, so the scores need no copy (the loop used
-          // to copy 48 of them a tile; measured 0.5-1.0% faster on the bf16 workloads)
+        if constexpr (!INT8K && H > 0) {
+          // bf16 keys, second key half: the exponent s * log2(e)/16 - m at once, reading
+          // the accumulators before this half's MFMAs reuse them, so the scores need no
+          // copy (the first half's exponents were formed during the last P·V steps)
 #pragma clang fp contract(off)
 #pragma unroll
           for (int b = 0; b < QB; ++b) {
@@ -1373,7 +1420,8 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
                 pq8[b][2 * H] = wv[0];
                 pq8[b][2 * H + 1] = wv[1];
               } else {
-                f32x8 pv;   // the exponents are ready (bf16 keys: computed with the scores above)
+                f32x8 pv;   // the exponents are ready (bf16 keys: the second half's computed
+                            // above, the first half's during the previous tile's P·V steps)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                   pv[e] = __builtin_amdgcn_exp2f(sc[b][e]);
@@ -1499,7 +1547,58 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
               constexpr bool kF = decltype(first_c)::value;
               constexpr int k = decltype(kc)::value;
               if constexpr (!INT8K) {
-                mfma_pv<kF>(acc, v, pp);
+                // bf16 keys: the exponents of S(j+1)'s first key half over the last 16
+                // gaps (ExpSchedule; two FMAs a gap with 3 query blocks). Measured in loop cycles a tile
+                // against forming them before that half's first Q·K^T MFMA, where they
+                // ran with no MFMA to overlap: 1.7% fewer on 4096 x 32768, 1.5% on
+                // 3072 x 16384, 0.2% on the paged 512 x 32768 tail (12 gaps: 1.4%, 1.2%,
+                // 0.3% more; 24 gaps, one a gap: 0.5%, 0.4%, 1.2% more; all 48 FMAs
+                // spread over the steps from step 2: 0.5% slower on 4096 x 32768).
+                constexpr int kStmts = kPvSteps * QB * (SPLIT ? 2 : 1);
+                using ES = ExpSchedule<kStmts, (kStmts - 1 < 16 ? kStmts - 1 : 16), 8 * QB>;
+                constexpr CarryPlan cp = ES::carries(k);
+                auto load = [&](auto ic) -> uint32_t {
+                  constexpr int kind = cp.kind[decltype(ic)::value], i = cp.score[decltype(ic)::value];
+                  constexpr int u = i / 4, kb = u / QB, b = u % QB, r = i % 4;
+                  // (the element read into a scalar first: this compiler's bit cast of a
+                  // vector element reads the vector's first element instead)
+                  const float x = kind == CarryPlan::kY ? sacc[b][kb][r] : m[b];
+                  return __builtin_bit_cast(uint32_t, x);
+                };
+                auto store = [&](auto ic, uint32_t w) {
+                  constexpr int kind = cp.kind[decltype(ic)::value], i = cp.score[decltype(ic)::value];
+                  constexpr int u = i / 4, kb = u / QB, b = u % QB, r = i % 4;
+                  if constexpr (kind == CarryPlan::kY) sacc[b][kb][r] = __builtin_bit_cast(float, w);
+                  else m[b] = __builtin_bit_cast(float, w);
+                };
+                using I0 = std::integral_constant<int, 0>;
+                using I1 = std::integral_constant<int, 1>;
+                using I2 = std::integral_constant<int, 2>;
+                if constexpr (cp.n == 0) {
+                  mfma_pv<kF>(acc, v, pp);
+                } else if constexpr (cp.n == 1) {
+                  uint32_t a = load(I0{});
+                  mfma_pv_carry<kF>(acc, v, pp, a);
+                  store(I0{}, a);
+                } else if constexpr (cp.n == 2) {
+                  uint32_t a = load(I0{}), b = load(I1{});
+                  mfma_pv_carry<kF>(acc, v, pp, a, b);
+                  store(I0{}, a);
+                  store(I1{}, b);
+                } else {
+                  static_assert(cp.n == 3, "at most 3 registers carried per statement");
+                  uint32_t a = load(I0{}), b = load(I1{}), c = load(I2{});
+                  mfma_pv_carry<kF>(acc, v, pp, a, b, c);
+                  store(I0{}, a);
+                  store(I1{}, b);
+                  store(I2{}, c);
+                }
+                static_for<ES::first_op(k), ES::first_op(k + 1)>([&](auto ic) {
+#pragma clang fp contract(off)
+                  constexpr int i = decltype(ic)::value;
+                  constexpr int u = i / 4, kb = u / QB, b = u % QB, r = i % 4;
+                  sacc[b][kb][r] = __builtin_fmaf(sacc[b][kb][r], kLog2eOver16, -m[b]);
+                });
               } else {
                 constexpr CarryPlan cp = SS::carries(k);
                 auto load = [&](auto ic) -> uint32_t {
