@@ -1391,7 +1391,8 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
         if constexpr (!INT8K && H > 0) {
           // bf16 keys, second key half: the exponent s * log2(e)/16 - m at once, reading
           // the accumulators before this half's MFMAs reuse them, so the scores need no
-          // copy (the first half's exponents were formed during the last P·V steps)
+          // copy (the first half's exponents were formed during the previous tile's last
+          // P·V steps)
 #pragma clang fp contract(off)
 #pragma unroll
           for (int b = 0; b < QB; ++b) {
@@ -1556,14 +1557,14 @@ __device__ __forceinline__ void run(const Params& p, uint8_t* smem) {
               constexpr int k = decltype(kc)::value;
               if constexpr (!INT8K) {
                 // bf16 keys: the exponents of S(j+1)'s first key half over the last 16
-                // gaps (ExpSchedule; two FMAs a gap with 3 query blocks). Measured in loop
-                // cycles a tile against forming them before that half's first Q·K^T MFMA,
-                // where they ran with no MFMA to overlap: 1.7% fewer on 4096 x 32768, 1.5%
-                // on 3072 x 16384, 0.2% on the paged 512 x 32768 tail (12 gaps: 1.5% and
-                // 1.2% fewer, 0.3% more; 24 gaps, one a gap: 0.5% and 0.4% fewer, 1.2%
-                // more; all 48 FMAs spread over the steps from step 2: 0.5% slower in time
-                // on 4096 x 32768). In time the gain is smaller (0.1-1.2%, same-box A/B):
-                // the chip holds the denser loop at a lower clock.
+                // gaps (ExpSchedule; one or two FMAs a gap with 3 query blocks). Measured in
+                // loop cycles a tile against forming them before that half's first Q·K^T
+                // MFMA, where they ran with no MFMA to overlap: 1.7% fewer on 4096 x 32768,
+                // 1.5% on 3072 x 16384, 0.2% on the paged 512 x 32768 tail (12 gaps, two a
+                // gap: 1.5% and 1.2% fewer, 0.3% more; 24 gaps, one a gap: 0.5% and 0.4%
+                // fewer, 1.2% more; all 48 FMAs spread over the steps from step 2: 0.5%
+                // slower in time on 4096 x 32768). In time the gain is smaller (0.1-1.2%,
+                // same-box A/B): the chip holds the denser loop at a lower clock.
                 constexpr int kStmts = kPvSteps * QB * (SPLIT ? 2 : 1);
                 using ES = ExpSchedule<kStmts, (kStmts - 1 < 16 ? kStmts - 1 : 16), 8 * QB>;
                 constexpr CarryPlan cp = ES::carries(k);
